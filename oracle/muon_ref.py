@@ -1,0 +1,336 @@
+"""Plain fp64 CPU reference of the Muon optimizer step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the test suite, the package's smoke check and the
+benchmark's CPU-baseline leg use it.  It shares no code with the HIP library
+(no kernels, headers, helpers or constants); the two meet only through the
+seeded input generators in ``workloads``.
+
+Every function is written from the pages in the order and notation they use,
+in float64, with numpy's matmul as the only library primitive.  There is no
+blocking, fusion or reordering beyond what the cited passage states.
+
+Sources (web pages; cited by title and section):
+  [Blog]      "Muon Optimizer and the Distributed Implementation" (blog.chensy.moe)
+  [Moonlight] the Kimi/Moonlight summary page ("...Muon优化器可替代 AdamW..."),
+              sections "权重衰减机制", "参数更新尺度调整:一致的更新 RMS" and "代码"
+              (the PyTorch ``Muon`` class printed there)
+  [DeepSpeed] "DeepSpeed 集成 Muon 优化器实战..." (NS_METHODS, Gram variant)
+  [MindSpeed] the MindSpeed "Muon 优化器" document (QKV split, 实现原理)
+
+Readings taken where the pages are silent or garbled are listed in the
+project's design notes; each function below states the one it relies on.
+
+Parity pins: every function here is pinned by tests against closed forms,
+hand-reduced cases, invariants or brute force (see tests/test_oracle_*.py).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+# [Blog] "Newton-Schulz Iteration": the quintic coefficients found by gradient
+# descent, used five times ("NewtonSchulz5").
+QUINTIC = (3.4445, -4.7750, 2.0315)
+DEFAULT_STEPS = 5
+# [Moonlight] "参数更新尺度调整": update RMS matched with the constant 0.2.
+RMS_SCALE = 0.2
+
+
+def coeff_schedule(steps: int, coeffs: Optional[Sequence] = None) -> List[Tuple[float, float, float]]:
+    """Per-step (a, b, c).  ``coeffs`` is None (the quintic every step), one
+    triple (used every step) or a list of ``steps`` triples."""
+    if coeffs is None:
+        return [QUINTIC] * steps
+    arr = np.asarray(coeffs, dtype=np.float64)
+    if arr.shape == (3,):
+        return [tuple(float(x) for x in arr)] * steps
+    if arr.shape != (steps, 3):
+        raise ValueError(f"coeffs must be (3,) or ({steps}, 3), got {arr.shape}")
+    return [tuple(float(x) for x in row) for row in arr]
+
+
+# --------------------------------------------------------------------------
+# Momentum  ([Blog] "Formulation of Muon Optimizer"; [Moonlight] "代码", step)
+# --------------------------------------------------------------------------
+
+def momentum_update(M: np.ndarray, G: np.ndarray, mu: float, nesterov: bool):
+    """M_t = mu*M_{t-1} + G_t; the matrix to orthogonalize is G_t + mu*M_t
+    with Nesterov ([Blog] "Variation of Muon Optimizer": msign(beta*M_t + G_t);
+    [Moonlight] code: ``buf.mul_(momentum).add_(g)`` then ``g.add(buf,
+    alpha=momentum)``), else M_t itself.  Returns (M_t, U)."""
+    M = np.asarray(M, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    M_new = mu * M + G
+    U = G + mu * M_new if nesterov else M_new.copy()
+    return M_new, U
+
+
+# --------------------------------------------------------------------------
+# Orthogonalization  ([Blog] "Orthogonalization of Gradients",
+# "Sign of a Matrix", "Newton-Schulz Iteration")
+# --------------------------------------------------------------------------
+
+def frobenius_normalize(X: np.ndarray):
+    """X / ||X||_F, which puts every singular value in [0, 1] ([Blog]
+    "Newton-Schulz Iteration", first added condition).  The page prints no
+    epsilon; the one reading taken is that a zero matrix stays zero (its
+    orthogonalized update is then zero).  Returns (X_normalized, s)."""
+    X = np.asarray(X, dtype=np.float64)
+    s = math.sqrt(float(np.sum(X * X)))
+    if s == 0.0:
+        return np.zeros_like(X), 0.0
+    return X / s, s
+
+
+def ns_standard(X: np.ndarray, schedule) -> np.ndarray:
+    """Newton-Schulz on a normalized X with rows <= cols.  Each step applies
+    phi(X) = (a + b X X^T + c (X X^T)^2) X ([Blog] "Newton-Schulz Iteration"),
+    evaluated in Horner form a X + (b A + c A A) X with A = X X^T, as the page
+    says implementations do."""
+    X = np.asarray(X, dtype=np.float64)
+    for a, b, c in schedule:
+        A = X @ X.T
+        B = b * A + c * (A @ A)
+        X = a * X + B @ X
+    return X
+
+
+def ns_gram(X: np.ndarray, schedule) -> np.ndarray:
+    """Gram variant ([DeepSpeed]: iterate on the small square Gram matrix
+    R = X X^T instead of the rectangular X).  The page describes only that;
+    the reading taken is the exact-arithmetic rewrite of ``ns_standard``:
+    with P_k = a I + b R_k + c R_k^2 one has X_{k+1} = P_k X_k, so
+    R_{k+1} = P_k R_k P_k and X_N = (P_{N-1} ... P_0) X_0 = Q X_0."""
+    X = np.asarray(X, dtype=np.float64)
+    m = X.shape[0]
+    I = np.eye(m)
+    R = X @ X.T
+    Q = I.copy()
+    steps = len(schedule)
+    for k, (a, b, c) in enumerate(schedule):
+        P = a * I + b * R + c * (R @ R)
+        Q = P @ Q
+        if k < steps - 1:
+            R = P @ R @ P
+    return Q @ X
+
+
+def orthogonalize(G: np.ndarray, steps: int = DEFAULT_STEPS, coeffs=None,
+                  method: str = "standard") -> np.ndarray:
+    """NewtonSchulz(G) for one logically independent matrix G (rows x cols).
+
+    A tall G is processed as its transpose: msign(G) = (G G^T)^{-1/2} G =
+    G (G^T G)^{-1/2} ([Blog] "Sign of a Matrix", first theorem), so the
+    iteration may run on whichever Gram side is smaller and the result is
+    transposed back.  Then Frobenius-normalize and iterate."""
+    G = np.asarray(G, dtype=np.float64)
+    if G.ndim != 2:
+        raise ValueError("orthogonalize expects a 2-D matrix")
+    rows, cols = G.shape
+    if rows == 0 or cols == 0:
+        return np.zeros_like(G)
+    tall = rows > cols
+    X = G.T if tall else G
+    X, s = frobenius_normalize(X)
+    if s == 0.0:
+        return np.zeros_like(G)
+    sched = coeff_schedule(steps, coeffs)
+    if method == "standard":
+        X = ns_standard(X, sched)
+    elif method == "gram":
+        X = ns_gram(X, sched)
+    else:
+        raise ValueError(f"unknown ns method {method!r}")
+    return X.T.copy() if tall else X
+
+
+def quintic_scalar(x: float, steps: int = DEFAULT_STEPS, coeffs=None) -> float:
+    """The scalar map each singular value undergoes: g(x) = a x + b x^3 + c x^5
+    applied ``steps`` times ([Blog] "Newton-Schulz Iteration": phi(G) =
+    U (a S + b S^3 + c S^5) V^T).  Used by closed-form checks."""
+    for a, b, c in coeff_schedule(steps, coeffs):
+        x = a * x + b * x ** 3 + c * x ** 5
+    return x
+
+
+# --------------------------------------------------------------------------
+# Update  ([Moonlight] "权重衰减机制", "参数更新尺度调整", "代码")
+# --------------------------------------------------------------------------
+
+def muon_scale(rows: int, cols: int, scale_dim: int = 0, rms_scale: float = RMS_SCALE) -> float:
+    """0.2 * sqrt(max(A, B)) ([Moonlight] "参数更新尺度调整"; the code's
+    ``adjust_lr_for_muon``).  For a split block the reading taken is the
+    block's own shape ([Blog] DeepSeek-V4 listing rescales each logically
+    independent weight by sqrt(max(n, m))); ``scale_dim`` > 0 overrides
+    max(A, B)."""
+    d = scale_dim if scale_dim > 0 else max(rows, cols)
+    return rms_scale * math.sqrt(d)
+
+
+def weight_update(W: np.ndarray, O: np.ndarray, lr: float, wd: float, scale: float) -> np.ndarray:
+    """W_t = W_{t-1} - lr * (scale * O_t + wd * W_{t-1}) ([Moonlight]
+    "参数更新尺度调整" update formula), as the code applies it:
+    ``p.mul_(1 - lr*wd)`` then ``p.add_(u, alpha=-lr*scale)``."""
+    W = np.asarray(W, dtype=np.float64)
+    return W * (1.0 - lr * wd) - (lr * scale) * np.asarray(O, dtype=np.float64)
+
+
+def adamw_update(W, g, m, v, t: int, lr: float, beta1: float, beta2: float,
+                 eps: float, wd: float):
+    """The AdamW fallback of the [Moonlight] code ("AdamW backup"), step t >= 1:
+    m <- lerp(m, g, 1-beta1); v <- lerp(v, g^2, 1-beta2);
+    u = m / (eps + sqrt(v)); scale = (1-beta1^t) / sqrt(1-beta2^t);
+    W <- W (1 - lr wd) - (lr / scale) u.  eps sits outside the bias
+    correction exactly as printed.  Returns (W, m, v)."""
+    W = np.asarray(W, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    m = np.asarray(m, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    m = m + (1.0 - beta1) * (g - m)
+    v = v + (1.0 - beta2) * (g * g - v)
+    u = m / (eps + np.sqrt(v))
+    bc1 = 1.0 - beta1 ** t
+    bc2 = 1.0 - beta2 ** t
+    scale = bc1 / math.sqrt(bc2)
+    W = W * (1.0 - lr * wd) - (lr / scale) * u
+    return W, m, v
+
+
+# --------------------------------------------------------------------------
+# Shape table -> units -> buckets  (independent brute-force planner)
+# --------------------------------------------------------------------------
+
+KIND_MUON = 0
+KIND_ADAMW = 1
+DT_F32 = 0
+DT_BF16 = 1
+
+
+@dataclass
+class OracleUnit:
+    param: int
+    row0: int
+    rows: int
+    cols: int
+    scale_dim: int
+
+    @property
+    def tall(self) -> bool:
+        return self.rows > self.cols
+
+    @property
+    def m(self) -> int:
+        return min(self.rows, self.cols)
+
+    @property
+    def n(self) -> int:
+        return max(self.rows, self.cols)
+
+
+def plan_units(table) -> List[OracleUnit]:
+    """Split each Muon parameter into its independent units, in table order.
+    A parameter with split_rows > 0 is cut into consecutive row blocks of that
+    height, each orthogonalized on its own ([MindSpeed] "QKV split": the fused
+    QKV weight is split into Q/K/V sub-matrices, each orthogonalized, then put
+    back; [DeepSpeed] per-attention-head "Muon Split")."""
+    units = []
+    for p, row in enumerate(table):
+        kind, dtype, rows, cols, split_rows, scale_dim = row
+        if kind != KIND_MUON or rows == 0 or cols == 0:
+            continue
+        h = split_rows if split_rows > 0 else rows
+        r = 0
+        while r < rows:
+            units.append(OracleUnit(p, r, h, cols, scale_dim))
+            r += h
+    return units
+
+
+def plan_buckets(table, method: int, ns_dtype: int = -1):
+    """Group units with the same (m, n, tall, compute dtype, method).  Buckets
+    are numbered by first appearance; units inside a bucket keep table order.
+    Brute force: for every unit, scan the buckets seen so far.  ``ns_dtype``
+    -1 means the compute dtype follows the parameter dtype."""
+    units = plan_units(table)
+    keys = []
+    members = []
+    for ui, u in enumerate(units):
+        dt = table[u.param][1] if ns_dtype < 0 else ns_dtype
+        key = (u.m, u.n, 1 if u.tall else 0, dt, method)
+        found = -1
+        for bi, k in enumerate(keys):
+            if k == key:
+                found = bi
+                break
+        if found < 0:
+            keys.append(key)
+            members.append([ui])
+        else:
+            members[found].append(ui)
+    return units, keys, members
+
+
+# --------------------------------------------------------------------------
+# Whole step over a shape table
+# --------------------------------------------------------------------------
+
+@dataclass
+class OracleHparams:
+    lr: float = 0.02
+    momentum: float = 0.95
+    weight_decay: float = 0.1
+    nesterov: bool = True
+    ns_steps: int = DEFAULT_STEPS
+    coeffs: Optional[Sequence] = None
+    rms_scale: float = RMS_SCALE
+    adam_lr: float = 3e-4
+    adam_beta1: float = 0.9
+    adam_beta2: float = 0.95
+    adam_eps: float = 1e-8
+    adam_weight_decay: float = 0.1
+    adam_step: int = 1
+
+
+def muon_step(table, params, grads, moms, exp_avgs, exp_avg_sqs, hp: OracleHparams,
+              method: str = "standard", units_subset: Optional[Sequence[int]] = None,
+              want_updates: bool = False):
+    """One optimizer step over a shape table (lists of fp64 arrays, updated
+    copies returned).  Muon parameters follow [Moonlight] "代码" step():
+    momentum, orthogonalize (per unit), weight decay then the scaled update;
+    the rest take the AdamW fallback.  ``units_subset`` restricts the Muon work
+    to those unit indices (the momentum of a parameter is updated only on the
+    rows of the selected units).  Returns dict with W, M, m, v lists and, if
+    asked, the per-unit orthogonalized update O."""
+    units = plan_units(table)
+    sel = range(len(units)) if units_subset is None else units_subset
+    W_out = [None if p is None else np.array(p, dtype=np.float64) for p in params]
+    M_out = [None if mm is None else np.array(mm, dtype=np.float64) for mm in moms]
+    ea_out = [None if x is None else np.array(x, dtype=np.float64) for x in exp_avgs]
+    es_out = [None if x is None else np.array(x, dtype=np.float64) for x in exp_avg_sqs]
+    updates = {}
+    for ui in sel:
+        u = units[ui]
+        r0, r1 = u.row0, u.row0 + u.rows
+        G = np.asarray(grads[u.param], dtype=np.float64)[r0:r1]
+        M = np.asarray(moms[u.param], dtype=np.float64)[r0:r1]
+        M_new, U = momentum_update(M, G, hp.momentum, hp.nesterov)
+        M_out[u.param][r0:r1] = M_new
+        O = orthogonalize(U, hp.ns_steps, hp.coeffs, method)
+        scale = muon_scale(u.rows, u.cols, u.scale_dim, hp.rms_scale)
+        W = np.asarray(params[u.param], dtype=np.float64)[r0:r1]
+        W_out[u.param][r0:r1] = weight_update(W, O, hp.lr, hp.weight_decay, scale)
+        if want_updates:
+            updates[ui] = O
+    for p, row in enumerate(table):
+        if row[0] != KIND_ADAMW:
+            continue
+        W, m, v = adamw_update(params[p], grads[p], exp_avgs[p], exp_avg_sqs[p],
+                               hp.adam_step, hp.adam_lr, hp.adam_beta1, hp.adam_beta2,
+                               hp.adam_eps, hp.adam_weight_decay)
+        W_out[p], ea_out[p], es_out[p] = W, m, v
+    return {"W": W_out, "M": M_out, "exp_avg": ea_out, "exp_avg_sq": es_out,
+            "O": updates, "units": units}
