@@ -1,0 +1,188 @@
+/*
+ * libmuon -- the Muon optimizer step on one AMD Instinct MI355X (gfx950).
+ *
+ * One call of muon_step() performs, for every 2-D hidden weight (or every
+ * independent row block of one), the momentum update, Frobenius
+ * normalization, the Newton-Schulz orthogonalization and the scaled,
+ * decoupled-weight-decay update; every other parameter takes the elementwise
+ * AdamW fallback.  All work is hand-written HIP for gfx950.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [Blog]      "Muon Optimizer and the Distributed Implementation"
+ *   [Moonlight] the Kimi/Moonlight summary page ("...Muon优化器可替代 AdamW..."),
+ *               sections "权重衰减机制", "参数更新尺度调整:一致的更新 RMS", "代码"
+ *   [DeepSpeed] "DeepSpeed 集成 Muon 优化器实战..." (NS_METHODS, Gram variant)
+ *   [MindSpeed] the MindSpeed "Muon 优化器" document (QKV split)
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers are HIP device addresses (e.g. torch tensors'
+ *     data_ptr()).  The caller owns every buffer and the stream; the library
+ *     never allocates device memory.  Scratch memory is the caller-provided
+ *     workspace whose size the *_workspace_bytes queries return.
+ *   - Matrices are row-major with a leading dimension equal to their column
+ *     count unless an ld argument says otherwise.
+ *   - Calls only enqueue work on the given stream (a hipStream_t passed as
+ *     void*, NULL = the default stream); they never synchronize the host.
+ *   - Every argument is validated on the host before the first launch; on any
+ *     error nothing is enqueued and a negative muon_status is returned.
+ *   - Non-finite values in the data are not checked; they propagate.
+ *   - A workspace may not be used by two calls that overlap in time.
+ */
+#ifndef LIBMUON_H
+#define LIBMUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MUON_OK = 0,
+  MUON_E_ARG = -1,       /* null/misaligned pointer, bad count, non-finite hparam */
+  MUON_E_SHAPE = -2,     /* negative size, split_rows not dividing rows, ... */
+  MUON_E_DTYPE = -3,     /* unknown dtype code */
+  MUON_E_METHOD = -4,    /* unknown ns_method */
+  MUON_E_WORKSPACE = -5, /* workspace null or smaller than required */
+  MUON_E_HIP = -6,       /* a HIP runtime call or kernel launch failed */
+  MUON_E_PLAN = -7,      /* plan and call disagree (table size, ...) */
+  MUON_E_CAPACITY = -8   /* output array too small (query calls) */
+} muon_status;
+
+/* [DeepSpeed] NS_METHODS = {standard, gram}. */
+typedef enum { MUON_NS_STANDARD = 0, MUON_NS_GRAM = 1 } muon_ns_method;
+
+/* Storage dtype of parameters and gradients.  Momentum and AdamW moments are
+ * always fp32. */
+typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype;
+
+/* [Moonlight] "代码": parameters tagged use_muon take the Muon rule, the rest
+ * (embeddings, heads, norms, biases) take the AdamW backup. */
+typedef enum { MUON_KIND_MUON = 0, MUON_KIND_ADAMW = 1 } muon_kind;
+
+/* One row of the shape table (plan time; no pointers).
+ *   rows, cols  the 2-D view of the parameter (callers flatten ndim > 2 as
+ *               [size(0), -1], as the [Moonlight] code does; vectors 1 x len).
+ *   split_rows  0: the whole matrix is one unit.  h > 0: rows must be a
+ *               multiple of h and each block of h consecutive rows is
+ *               orthogonalized on its own ([MindSpeed] QKV split; per-head
+ *               split).  Muon kind only.
+ *   scale_dim   0: the update scale is rms_scale*sqrt(max(unit rows, cols));
+ *               d > 0: rms_scale*sqrt(d) ([Moonlight] "参数更新尺度调整"). */
+typedef struct {
+  int32_t kind;   /* muon_kind */
+  int32_t dtype;  /* muon_dtype of param and grad */
+  int64_t rows;
+  int64_t cols;
+  int64_t split_rows;
+  int64_t scale_dim;
+} muon_param_shape;
+
+/* Device pointers of one parameter for one step (same order as the table).
+ *   param     rows x cols, dtype; updated in place.
+ *   grad      rows x cols, dtype; read only.
+ *   momentum  rows x cols fp32 (Muon kind); updated in place.
+ *   exp_avg, exp_avg_sq  rows x cols fp32 (AdamW kind); updated in place.
+ *   update_out  optional (may be NULL), Muon kind: rows x cols fp32 receives
+ *             the orthogonalized update O of every unit (before scaling).
+ * Alignment: param/grad to their element size, fp32 buffers to 4 bytes. */
+typedef struct {
+  void* param;
+  const void* grad;
+  float* momentum;
+  float* exp_avg;
+  float* exp_avg_sq;
+  float* update_out;
+} muon_param_ptrs;
+
+/* Hyperparameters of one step.
+ *   lr, momentum, weight_decay, nesterov, ns_steps: the Muon rule
+ *     ([Blog] "Formulation of Muon Optimizer"; [Moonlight] "权重衰减机制").
+ *   coeffs: host array of ns_steps*3 floats (a_k, b_k, c_k) or NULL for the
+ *     quintic (3.4445, -4.7750, 2.0315) at every step ([Blog] "Newton-Schulz
+ *     Iteration").
+ *   rms_scale: 0.2 in [Moonlight]; the update is
+ *     W <- W (1 - lr wd) - lr rms_scale sqrt(max(A,B)) O.
+ *   adam_*: the AdamW backup of the [Moonlight] code; adam_step is t >= 1
+ *     (already incremented): W <- W (1 - lr wd) - lr sqrt(1-b2^t)/(1-b1^t) *
+ *     m / (eps + sqrt(v)). */
+typedef struct {
+  float lr;
+  float momentum;
+  float weight_decay;
+  int32_t nesterov;
+  int32_t ns_steps;
+  const float* coeffs;
+  float rms_scale;
+  float adam_lr;
+  float adam_beta1;
+  float adam_beta2;
+  float adam_eps;
+  float adam_weight_decay;
+  int64_t adam_step;
+} muon_hparams;
+
+/* Plan options.
+ *   ns_method  muon_ns_method.
+ *   ns_dtype   -1: Newton-Schulz computes in the parameter dtype (bf16 MFMA
+ *              for bf16 parameters, fp32 MFMA for fp32 ones); MUON_F32 or
+ *              MUON_BF16 forces one. */
+typedef struct {
+  int32_t ns_method;
+  int32_t ns_dtype;
+} muon_plan_options;
+
+typedef struct muon_plan muon_plan;
+
+/* Build an immutable plan from a shape table of n rows: units (one per
+ * matrix or row block) grouped into buckets of equal (m, n, tall, parameter
+ * dtype, compute dtype, method), m = min and n = max of the unit's sides.
+ * Buckets are numbered by first appearance; units keep table order.  Host
+ * only (no HIP call).  *out receives a heap object to release with
+ * muon_plan_destroy.  Errors: MUON_E_ARG (null out, n < 0, unknown kind),
+ * MUON_E_DTYPE, MUON_E_METHOD, MUON_E_SHAPE (negative size, side > 2^30,
+ * split_rows not dividing rows or set on an AdamW row). */
+muon_status muon_plan_create(const muon_param_shape* table, int32_t n,
+                             const muon_plan_options* opts, muon_plan** out);
+void muon_plan_destroy(muon_plan* plan);
+
+/* Bytes of device workspace muon_step needs with this plan. */
+muon_status muon_plan_workspace_bytes(const muon_plan* plan, size_t* bytes);
+
+/* Bit-exact view of the plan (host only).  Buckets: 8 int32 per bucket
+ * (m, n, tall, param dtype, compute dtype, method, first unit, unit count);
+ * units, listed bucket by bucket: 6 int64 per unit (param, row0, rows, cols,
+ * tall, scale_dim as resolved).  *len receives the number of values needed;
+ * with out == NULL and cap == 0 this is a size query (MUON_OK), otherwise a
+ * cap below it returns MUON_E_CAPACITY and writes nothing. */
+muon_status muon_plan_buckets(const muon_plan* plan, int32_t* out, size_t cap, size_t* len);
+muon_status muon_plan_units(const muon_plan* plan, int64_t* out, size_t cap, size_t* len);
+
+/* One optimizer step for every parameter of the plan's table (n must equal
+ * the table size).  Enqueues on stream; all state is updated in place. */
+muon_status muon_step(const muon_plan* plan, const muon_param_ptrs* ptrs, int32_t n,
+                      const muon_hparams* hp, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* Newton-Schulz orthogonalization of one matrix X (rows x cols, leading
+ * dimension ld >= cols, dtype MUON_F32 or MUON_BF16), in place:
+ * X <- NS_steps(X / ||X||_F), a tall X being processed as its transpose
+ * ([Blog] "Sign of a Matrix", "Newton-Schulz Iteration").  coeffs as in
+ * muon_hparams.  A zero matrix stays zero. */
+muon_status ns_orthogonalize(void* X, int64_t rows, int64_t cols, int64_t ld, int32_t dtype,
+                             int32_t steps, const float* coeffs, int32_t method,
+                             void* workspace, size_t workspace_bytes, void* stream);
+muon_status ns_orthogonalize_workspace_bytes(int64_t rows, int64_t cols, int32_t dtype,
+                                             int32_t method, size_t* bytes);
+
+/* Static text for a status code. */
+const char* muon_status_string(int32_t status);
+
+/* Library version (major*10000 + minor*100 + patch). */
+int32_t muon_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMUON_H */

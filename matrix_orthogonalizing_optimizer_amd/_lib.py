@@ -1,0 +1,254 @@
+"""ctypes binding of libmuon (include/libmuon.h).  Argument marshalling only:
+every step of the optimizer runs in the library's HIP kernels.  Torch
+tensors are accepted for device memory (their data_ptr()) and the current
+HIP stream; nothing here computes on them.
+
+There is no fallback: if libmuon.so is missing or fails to load, every call
+raises."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmuon.so")
+
+MUON_OK = 0
+STATUS = {0: "MUON_OK", -1: "MUON_E_ARG", -2: "MUON_E_SHAPE", -3: "MUON_E_DTYPE",
+          -4: "MUON_E_METHOD", -5: "MUON_E_WORKSPACE", -6: "MUON_E_HIP", -7: "MUON_E_PLAN",
+          -8: "MUON_E_CAPACITY"}
+MUON_NS_STANDARD, MUON_NS_GRAM = 0, 1
+MUON_F32, MUON_BF16 = 0, 1
+MUON_KIND_MUON, MUON_KIND_ADAMW = 0, 1
+
+EXPORTED = ["muon_plan_create", "muon_plan_destroy", "muon_plan_workspace_bytes",
+            "muon_plan_buckets", "muon_plan_units", "muon_step", "ns_orthogonalize",
+            "ns_orthogonalize_workspace_bytes", "muon_status_string", "muon_version"]
+
+
+class MuonError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({status})")
+
+
+class MuonParamShape(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("dtype", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("split_rows", ctypes.c_int64), ("scale_dim", ctypes.c_int64)]
+
+
+class MuonParamPtrs(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("momentum", ctypes.c_void_p),
+                ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p),
+                ("update_out", ctypes.c_void_p)]
+
+
+class MuonHparams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_float), ("momentum", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("nesterov", ctypes.c_int32), ("ns_steps", ctypes.c_int32),
+                ("coeffs", ctypes.POINTER(ctypes.c_float)), ("rms_scale", ctypes.c_float),
+                ("adam_lr", ctypes.c_float), ("adam_beta1", ctypes.c_float),
+                ("adam_beta2", ctypes.c_float), ("adam_eps", ctypes.c_float),
+                ("adam_weight_decay", ctypes.c_float), ("adam_step", ctypes.c_int64)]
+
+
+class MuonPlanOptions(ctypes.Structure):
+    _fields_ = [("ns_method", ctypes.c_int32), ("ns_dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libmuon.so from the package directory (raises if absent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libmuon.so not built at {LIB_PATH}; run "
+                           "python -m matrix_orthogonalizing_optimizer_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.muon_plan_create.argtypes = [ctypes.POINTER(MuonParamShape), i32, ctypes.POINTER(MuonPlanOptions),
+                                   ctypes.POINTER(vp)]
+    L.muon_plan_create.restype = i32
+    L.muon_plan_destroy.argtypes = [vp]
+    L.muon_plan_destroy.restype = None
+    L.muon_plan_workspace_bytes.argtypes = [vp, ctypes.POINTER(sz)]
+    L.muon_plan_workspace_bytes.restype = i32
+    L.muon_plan_buckets.argtypes = [vp, ctypes.POINTER(i32), sz, ctypes.POINTER(sz)]
+    L.muon_plan_buckets.restype = i32
+    L.muon_plan_units.argtypes = [vp, ctypes.POINTER(i64), sz, ctypes.POINTER(sz)]
+    L.muon_plan_units.restype = i32
+    L.muon_step.argtypes = [vp, ctypes.POINTER(MuonParamPtrs), i32, ctypes.POINTER(MuonHparams), vp, sz, vp]
+    L.muon_step.restype = i32
+    L.ns_orthogonalize.argtypes = [vp, i64, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float), i32, vp,
+                                   sz, vp]
+    L.ns_orthogonalize.restype = i32
+    L.ns_orthogonalize_workspace_bytes.argtypes = [i64, i64, i32, i32, ctypes.POINTER(sz)]
+    L.ns_orthogonalize_workspace_bytes.restype = i32
+    L.muon_status_string.argtypes = [i32]
+    L.muon_status_string.restype = ctypes.c_char_p
+    L.muon_version.argtypes = []
+    L.muon_version.restype = i32
+    _lib = L
+    return L
+
+
+def _check(fn, st):
+    if st != MUON_OK:
+        raise MuonError(fn, st)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _coeff_array(coeffs, steps):
+    if coeffs is None:
+        return None
+    flat = []
+    if len(coeffs) == 3 and not hasattr(coeffs[0], "__len__"):
+        coeffs = [coeffs] * steps
+    for row in coeffs:
+        flat.extend(float(x) for x in row)
+    return (ctypes.c_float * len(flat))(*flat)
+
+
+class Plan:
+    """Owns a muon_plan handle (released on close / garbage collection)."""
+
+    def __init__(self, handle: int, table):
+        self.handle = handle
+        self.table = list(table)
+
+    def close(self):
+        if self.handle:
+            lib().muon_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def muon_plan_create(table: Sequence[Sequence[int]], ns_method: int = MUON_NS_STANDARD,
+                     ns_dtype: int = -1) -> Plan:
+    """table rows: (kind, dtype, rows, cols, split_rows, scale_dim)."""
+    n = len(table)
+    arr = (MuonParamShape * max(n, 1))()
+    for i, r in enumerate(table):
+        arr[i] = MuonParamShape(*[int(x) for x in r])
+    opts = MuonPlanOptions(int(ns_method), int(ns_dtype))
+    h = ctypes.c_void_p()
+    _check("muon_plan_create", lib().muon_plan_create(arr, n, ctypes.byref(opts), ctypes.byref(h)))
+    return Plan(h.value, table)
+
+
+def muon_plan_workspace_bytes(plan: Plan) -> int:
+    b = ctypes.c_size_t()
+    _check("muon_plan_workspace_bytes", lib().muon_plan_workspace_bytes(plan.handle, ctypes.byref(b)))
+    return b.value
+
+
+def muon_plan_buckets(plan: Plan) -> List[tuple]:
+    """[(m, n, tall, param_dtype, compute_dtype, method, first_unit, count), ...]"""
+    ln = ctypes.c_size_t()
+    _check("muon_plan_buckets", lib().muon_plan_buckets(plan.handle, None, 0, ctypes.byref(ln)))
+    buf = (ctypes.c_int32 * max(ln.value, 1))()
+    _check("muon_plan_buckets", lib().muon_plan_buckets(plan.handle, buf, ln.value, ctypes.byref(ln)))
+    return [tuple(buf[i:i + 8]) for i in range(0, ln.value, 8)]
+
+
+def muon_plan_units(plan: Plan) -> List[tuple]:
+    """[(param, row0, rows, cols, tall, scale_dim), ...] in bucket order."""
+    ln = ctypes.c_size_t()
+    _check("muon_plan_units", lib().muon_plan_units(plan.handle, None, 0, ctypes.byref(ln)))
+    buf = (ctypes.c_int64 * max(ln.value, 1))()
+    _check("muon_plan_units", lib().muon_plan_units(plan.handle, buf, ln.value, ctypes.byref(ln)))
+    return [tuple(buf[i:i + 6]) for i in range(0, ln.value, 6)]
+
+
+def make_hparams(lr=0.02, momentum=0.95, weight_decay=0.1, nesterov=True, ns_steps=5, coeffs=None,
+                 rms_scale=0.2, adam_lr=3e-4, adam_beta1=0.9, adam_beta2=0.95, adam_eps=1e-8,
+                 adam_weight_decay=0.1, adam_step=1):
+    ca = _coeff_array(coeffs, ns_steps)
+    hp = MuonHparams(lr, momentum, weight_decay, 1 if nesterov else 0, ns_steps,
+                     ctypes.cast(ca, ctypes.POINTER(ctypes.c_float)) if ca is not None else None,
+                     rms_scale, adam_lr, adam_beta1, adam_beta2, adam_eps, adam_weight_decay, adam_step)
+    hp._keep = ca  # keep the coefficient array alive with the struct
+    return hp
+
+
+def muon_step(plan: Plan, params, grads, moms, exp_avgs, exp_avg_sqs, hp: MuonHparams, workspace,
+              stream=None, update_outs=None) -> None:
+    """One optimizer step; lists follow the plan's table order (None where a
+    buffer does not apply).  workspace: a device tensor (or pointer) of at
+    least muon_plan_workspace_bytes(plan) bytes."""
+    n = len(plan.table)
+    arr = (MuonParamPtrs * max(n, 1))()
+    for i in range(n):
+        arr[i] = MuonParamPtrs(_ptr(params[i]), _ptr(grads[i]), _ptr(moms[i]), _ptr(exp_avgs[i]),
+                               _ptr(exp_avg_sqs[i]),
+                               _ptr(update_outs[i]) if update_outs is not None else None)
+    wsz = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
+    if isinstance(workspace, tuple):
+        workspace, wsz = workspace
+    _check("muon_step", lib().muon_step(plan.handle, arr, n, ctypes.byref(hp), _ptr(workspace), wsz,
+                                        _stream(stream)))
+
+
+def ns_orthogonalize_workspace_bytes(rows: int, cols: int, dtype: int, method: int = MUON_NS_STANDARD) -> int:
+    b = ctypes.c_size_t()
+    _check("ns_orthogonalize_workspace_bytes",
+           lib().ns_orthogonalize_workspace_bytes(rows, cols, dtype, method, ctypes.byref(b)))
+    return b.value
+
+
+def ns_orthogonalize(X, steps: int = 5, coeffs=None, method: int = MUON_NS_STANDARD, workspace=None,
+                     stream=None, rows=None, cols=None, ld=None, dtype=None) -> None:
+    """In place: X <- NewtonSchulz(X / ||X||_F).  X: a 2-D device tensor
+    (fp32 or bf16, rows may be strided) or a raw pointer with rows/cols/ld/dtype."""
+    if hasattr(X, "data_ptr"):
+        import torch
+        if X.dim() != 2 or X.stride(1) != 1:
+            raise ValueError("X must be 2-D with unit column stride")
+        rows, cols = X.shape
+        ld = X.stride(0) if rows > 1 else cols
+        dtype = MUON_F32 if X.dtype == torch.float32 else MUON_BF16
+        if X.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError("X must be float32 or bfloat16")
+        if workspace is None:
+            nb = ns_orthogonalize_workspace_bytes(rows, cols, dtype, method)
+            workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=X.device)
+    ca = _coeff_array(coeffs, steps)
+    wsz = workspace.numel() if hasattr(workspace, "numel") else 0
+    if isinstance(workspace, tuple):
+        workspace, wsz = workspace
+    _check("ns_orthogonalize",
+           lib().ns_orthogonalize(_ptr(X), rows, cols, ld, dtype, steps,
+                                  ca, method, _ptr(workspace), wsz, _stream(stream)))
+
+
+def muon_status_string(status: int) -> str:
+    return lib().muon_status_string(status).decode()
+
+
+def muon_version() -> int:
+    return lib().muon_version()

@@ -1,0 +1,531 @@
+// C ABI of libmuon: validation, workspace layout and the launch sequence of
+// one Muon optimizer step.
+//
+// Per bucket chunk (units of one shape), standard method ("Muon Optimizer and
+// the Distributed Implementation", sections "Formulation of Muon Optimizer"
+// and "Newton-Schulz Iteration"):
+//   K-M    M <- mu M + G;  U = G + mu M (Nesterov) or M;  X0 = U (wide layout)
+//          and partial sums of U^2                      [momentum_kernel]
+//   norm   s^2 per unit, 1/s, 1/s^2                      [norm_finalize_kernel]
+//   k = 0..steps-1 with (a_k, b_k, c_k):
+//     A = X X^T            (k = 0: times 1/s^2, folding X0 = U / s)
+//     B = c A A + b A      (symmetric: upper tiles, mirror-written)
+//     X' = a X + B X       (k = 0: times 1/s); the last step's epilogue
+//                          applies W <- W (1 - lr wd) - lr scale O directly
+// Gram method (DeepSpeed page: iterate on the square Gram matrix R = X X^T):
+//   R = 2^e X0 X0^T / s^2 (power-of-two scaled, fp16 for a bf16 bucket);
+//   P_k = a I + b R + c R^2;  Q <- P_k Q;  R <- P_k R P_k;  O = Q X0 / s.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "consts.hpp"
+#include "launch.hpp"
+#include "libmuon.h"
+#include "plan.hpp"
+
+using namespace muon;
+
+namespace {
+
+constexpr float kQuintic[3] = {3.4445f, -4.7750f, 2.0315f};
+
+struct ChainParams {
+  float mu;
+  int32_t nesterov;
+  int32_t steps;
+  const float* coeffs;  // steps x 3
+  float lr, wd;
+  int32_t final_mode;
+  int32_t vec_ok;
+};
+
+int dt_dev(int32_t muon_dtype) { return muon_dtype == MUON_F32 ? DT_F32 : DT_BF16; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+GemmArgs gemm_args(int tile, int32_t cnt, int M, int N, int K, bool sym) {
+  GemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.units = cnt;
+  g.tilesM = (int32_t)ceil_div(M, tile);
+  g.tilesN = (int32_t)ceil_div(N, tile);
+  g.tilesPerUnit = sym ? g.tilesM * (g.tilesM + 1) / 2 : g.tilesM * g.tilesN;
+  g.totalTiles = g.tilesPerUnit * cnt;
+  g.alpha = 1.f;
+  return g;
+}
+
+#define HIP_TRY(x)                          \
+  do {                                      \
+    hipError_t e_ = (x);                    \
+    if (e_ != hipSuccess) return MUON_E_HIP; \
+  } while (0)
+
+// Momentum + norm for one chunk, then the Newton-Schulz chain and the fused
+// update (or plain store of O for ns_orthogonalize).
+muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux, float* d_part,
+                      char* data, int32_t cnt, const ChainParams& cp, hipStream_t st) {
+  const int cdt = dt_dev(b.cdtype);
+  const int pdt = dt_dev(b.pdtype);
+  const int es = elem_size(b.cdtype);
+  const int64_t m = b.m, n = b.n;
+  const int64_t sx = m * b.ldx, ss = m * b.mp;
+
+  MomArgs ma;
+  std::memset(&ma, 0, sizeof(ma));
+  ma.desc = d_desc;
+  ma.X0 = data + b.off[0];
+  ma.ldx = b.ldx;
+  ma.sX = sx;
+  ma.partials = d_part;
+  ma.rows = (int32_t)(b.tall ? n : m);
+  ma.cols = (int32_t)(b.tall ? m : n);
+  ma.tilesR = (int32_t)ceil_div(ma.rows, KM_TR);
+  ma.tilesC = (int32_t)ceil_div(ma.cols, KM_TC);
+  ma.tilesPerUnit = b.km_tiles;
+  ma.mu = cp.mu;
+  ma.nesterov = cp.nesterov;
+  ma.vec_ok = cp.vec_ok;
+  HIP_TRY(launch_momentum(pdt, cdt, b.tall != 0, ma, (int64_t)cnt * b.km_tiles, st));
+  HIP_TRY(launch_norm_finalize(d_part, b.km_tiles, d_aux, cnt, st));
+
+  const int T = b.tile;
+  auto final_args = [&](GemmArgs& g) {
+    g.desc = d_desc;
+    g.lr = cp.lr;
+    g.wd = cp.wd;
+    g.finalMode = cp.final_mode;
+    g.tall = b.tall;
+    g.wdtype = pdt;
+  };
+
+  if (b.method == MUON_NS_STANDARD) {
+    char* X[2] = {data + b.off[0], data + b.off[1]};
+    char* A = data + b.off[2];
+    char* B = data + b.off[3];
+    for (int k = 0; k < cp.steps; ++k) {
+      const float ca = cp.coeffs[3 * k], cb = cp.coeffs[3 * k + 1], cc = cp.coeffs[3 * k + 2];
+      char* Xi = X[k & 1];
+      char* Xo = X[(k + 1) & 1];
+      // A = X X^T  (k = 0: U U^T / s^2)
+      GemmArgs g = gemm_args(T, cnt, (int)m, (int)m, (int)n, true);
+      g.L = Xi; g.ldl = b.ldx; g.sL = sx;
+      g.R = Xi; g.ldr = b.ldx; g.sR = sx;
+      g.C = A; g.ldc = b.mp; g.sC = ss;
+      g.alphaSel = k == 0 ? SEL_INV_S2 : SEL_ONE;
+      g.aux = d_aux;
+      HIP_TRY(launch_gemm(T, cdt, cdt, false, true, EPI_SCALE, g, st));
+      // B = c A A + b A
+      g = gemm_args(T, cnt, (int)m, (int)m, (int)m, true);
+      g.L = A; g.ldl = b.mp; g.sL = ss;
+      g.R = A; g.ldr = b.mp; g.sR = ss;
+      g.E = A; g.lde = b.mp; g.sE = ss;
+      g.C = B; g.ldc = b.mp; g.sC = ss;
+      g.alpha = cc; g.beta = cb; g.gamma = 0.f;
+      HIP_TRY(launch_gemm(T, cdt, cdt, false, true, EPI_POLY, g, st));
+      // X' = a X + B X  (k = 0: (a U + B U) / s)
+      g = gemm_args(T, cnt, (int)m, (int)n, (int)m, false);
+      g.L = B; g.ldl = b.mp; g.sL = ss;
+      g.R = Xi; g.ldr = b.ldx; g.sR = sx;
+      g.E = Xi; g.lde = b.ldx; g.sE = sx;
+      g.C = Xo; g.ldc = b.ldx; g.sC = sx;
+      g.alpha = 1.f; g.beta = ca;
+      g.alphaSel = k == 0 ? SEL_INV_S : SEL_ONE;
+      g.aux = d_aux;
+      if (k + 1 < cp.steps) {
+        HIP_TRY(launch_gemm(T, cdt, cdt, true, false, EPI_AXPY, g, st));
+      } else {
+        final_args(g);
+        HIP_TRY(launch_gemm(T, cdt, cdt, true, false, EPI_FINAL, g, st));
+      }
+    }
+    return MUON_OK;
+  }
+
+  // Gram chain: m x m work in fp16 (bf16 bucket) or fp32, R scaled by 2^e.
+  const int sdt = cdt == DT_F32 ? DT_F32 : DT_F16;
+  const int qdt_last = cdt == DT_F32 ? DT_F32 : DT_BF16;  // Q feeds the final GEMM with X0
+  float rs = 1.f;
+  if (sdt == DT_F16) {
+    int e = 0;
+    while ((int64_t(1) << e) < m && e < 15) ++e;
+    rs = std::ldexp(1.f, e);
+  }
+  char* X0 = data + b.off[0];
+  char* R = data + b.off[1];
+  char* Tm = data + b.off[2];
+  char* QP[3] = {data + b.off[3], data + b.off[4], data + b.off[5]};
+  (void)es;
+  GemmArgs g = gemm_args(T, cnt, (int)m, (int)m, (int)n, true);
+  g.L = X0; g.ldl = b.ldx; g.sL = sx;
+  g.R = X0; g.ldr = b.ldx; g.sR = sx;
+  g.C = R; g.ldc = b.mp; g.sC = ss;
+  g.alpha = rs; g.alphaSel = SEL_INV_S2; g.aux = d_aux;
+  HIP_TRY(launch_gemm(T, cdt, sdt, false, true, EPI_SCALE, g, st));
+  int q = -1;  // index of the buffer holding Q
+  for (int k = 0; k < cp.steps; ++k) {
+    const bool last = k + 1 == cp.steps;
+    const float ca = cp.coeffs[3 * k], cb = cp.coeffs[3 * k + 1], cc = cp.coeffs[3 * k + 2];
+    int p = 0;
+    while (p == q) ++p;
+    // P = a I + (b / rs) R + (c / rs^2) R R
+    g = gemm_args(T, cnt, (int)m, (int)m, (int)m, true);
+    g.L = R; g.ldl = b.mp; g.sL = ss;
+    g.R = R; g.ldr = b.mp; g.sR = ss;
+    g.E = R; g.lde = b.mp; g.sE = ss;
+    g.C = QP[p]; g.ldc = b.mp; g.sC = ss;
+    g.alpha = cc / (rs * rs); g.beta = cb / rs; g.gamma = ca;
+    HIP_TRY(launch_gemm(T, sdt, (last && k == 0) ? qdt_last : sdt, false, true, EPI_POLY, g, st));
+    if (k == 0) {
+      q = p;
+    } else {
+      int qn = 0;
+      while (qn == q || qn == p) ++qn;
+      // Q' = P Q
+      g = gemm_args(T, cnt, (int)m, (int)m, (int)m, false);
+      g.L = QP[p]; g.ldl = b.mp; g.sL = ss;
+      g.R = QP[q]; g.ldr = b.mp; g.sR = ss;
+      g.C = QP[qn]; g.ldc = b.mp; g.sC = ss;
+      g.beta = 0.f;
+      HIP_TRY(launch_gemm(T, sdt, last ? qdt_last : sdt, true, false, EPI_AXPY, g, st));
+      q = qn;
+    }
+    if (!last) {
+      // Tm = P R  (R symmetric: read as R^T rows)
+      g = gemm_args(T, cnt, (int)m, (int)m, (int)m, false);
+      g.L = QP[p]; g.ldl = b.mp; g.sL = ss;
+      g.R = R; g.ldr = b.mp; g.sR = ss;
+      g.C = Tm; g.ldc = b.mp; g.sC = ss;
+      g.beta = 0.f;
+      HIP_TRY(launch_gemm(T, sdt, sdt, false, false, EPI_AXPY, g, st));
+      // R = Tm P  (P symmetric; result symmetric: upper tiles + mirror)
+      g = gemm_args(T, cnt, (int)m, (int)m, (int)m, true);
+      g.L = Tm; g.ldl = b.mp; g.sL = ss;
+      g.R = QP[p]; g.ldr = b.mp; g.sR = ss;
+      g.C = R; g.ldc = b.mp; g.sC = ss;
+      HIP_TRY(launch_gemm(T, sdt, sdt, false, true, EPI_SCALE, g, st));
+    }
+  }
+  // O = Q X0 / s, fused with the update
+  g = gemm_args(T, cnt, (int)m, (int)n, (int)m, false);
+  g.L = QP[q]; g.ldl = b.mp; g.sL = ss;
+  g.R = X0; g.ldr = b.ldx; g.sR = sx;
+  g.E = X0; g.lde = b.ldx; g.sE = sx;
+  g.beta = 0.f;
+  g.alphaSel = SEL_INV_S;
+  g.aux = d_aux;
+  final_args(g);
+  HIP_TRY(launch_gemm(T, cdt, cdt, true, false, EPI_FINAL, g, st));
+  return MUON_OK;
+}
+
+bool finite(float x) { return std::isfinite(x); }
+
+muon_status coeff_table(int32_t steps, const float* coeffs, std::vector<float>& out) {
+  if (steps < 1 || steps > MAX_NS_STEPS) return MUON_E_ARG;
+  out.resize((size_t)steps * 3);
+  for (int k = 0; k < steps; ++k)
+    for (int j = 0; j < 3; ++j) {
+      const float v = coeffs ? coeffs[3 * k + j] : kQuintic[j];
+      if (!finite(v)) return MUON_E_ARG;
+      out[(size_t)3 * k + j] = v;
+    }
+  return MUON_OK;
+}
+
+char* align_base(void* p) {
+  const uintptr_t u = reinterpret_cast<uintptr_t>(p);
+  return reinterpret_cast<char*>((u + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN);
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t muon_version(void) { return 100; }
+
+const char* muon_status_string(int32_t s) {
+  switch (s) {
+    case MUON_OK: return "ok";
+    case MUON_E_ARG: return "invalid argument";
+    case MUON_E_SHAPE: return "invalid shape";
+    case MUON_E_DTYPE: return "invalid dtype";
+    case MUON_E_METHOD: return "invalid ns_method";
+    case MUON_E_WORKSPACE: return "workspace missing or too small";
+    case MUON_E_HIP: return "HIP runtime error";
+    case MUON_E_PLAN: return "plan and call disagree";
+    case MUON_E_CAPACITY: return "output array too small";
+  }
+  return "unknown status";
+}
+
+muon_status muon_plan_create(const muon_param_shape* table, int32_t n, const muon_plan_options* opts,
+                             muon_plan** out) {
+  if (!out) return MUON_E_ARG;
+  *out = nullptr;
+  muon_plan* p = new (std::nothrow) muon_plan;
+  if (!p) return MUON_E_ARG;
+  const muon_status st = build_plan(table, n, opts, p->impl);
+  if (st != MUON_OK) {
+    delete p;
+    return st;
+  }
+  *out = p;
+  return MUON_OK;
+}
+
+void muon_plan_destroy(muon_plan* plan) { delete plan; }
+
+muon_status muon_plan_workspace_bytes(const muon_plan* plan, size_t* bytes) {
+  if (!plan || !bytes) return MUON_E_ARG;
+  *bytes = plan->impl.lay.total;
+  return MUON_OK;
+}
+
+muon_status muon_plan_buckets(const muon_plan* plan, int32_t* out, size_t cap, size_t* len) {
+  if (!plan || !len) return MUON_E_ARG;
+  const auto& B = plan->impl.buckets;
+  const size_t need = B.size() * 8;
+  *len = need;
+  if (cap < need) return out || cap ? MUON_E_CAPACITY : MUON_OK;
+  if (!out && need) return MUON_E_ARG;
+  for (size_t i = 0; i < B.size(); ++i) {
+    const int32_t v[8] = {B[i].m, B[i].n, B[i].tall, B[i].pdtype, B[i].cdtype, B[i].method,
+                          B[i].first, B[i].count};
+    std::memcpy(out + 8 * i, v, sizeof(v));
+  }
+  return MUON_OK;
+}
+
+muon_status muon_plan_units(const muon_plan* plan, int64_t* out, size_t cap, size_t* len) {
+  if (!plan || !len) return MUON_E_ARG;
+  const auto& U = plan->impl.units;
+  const size_t need = U.size() * 6;
+  *len = need;
+  if (cap < need) return out || cap ? MUON_E_CAPACITY : MUON_OK;
+  if (!out && need) return MUON_E_ARG;
+  for (size_t i = 0; i < U.size(); ++i) {
+    const int64_t v[6] = {U[i].param, U[i].row0, U[i].rows, U[i].cols, U[i].tall, U[i].scale_dim};
+    std::memcpy(out + 6 * i, v, sizeof(v));
+  }
+  return MUON_OK;
+}
+
+muon_status muon_step(const muon_plan* plan, const muon_param_ptrs* ptrs, int32_t n,
+                      const muon_hparams* hp, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan || !hp) return MUON_E_ARG;
+  const PlanImpl& P = plan->impl;
+  if (n != (int32_t)P.table.size()) return MUON_E_PLAN;
+  if (n > 0 && !ptrs) return MUON_E_ARG;
+  std::vector<float> coeffs;
+  muon_status st = coeff_table(hp->ns_steps, hp->coeffs, coeffs);
+  if (st != MUON_OK) return st;
+  if (!finite(hp->lr) || !finite(hp->momentum) || !finite(hp->weight_decay) || !finite(hp->rms_scale))
+    return MUON_E_ARG;
+  if (!P.adam.empty()) {
+    if (!finite(hp->adam_lr) || !finite(hp->adam_beta1) || !finite(hp->adam_beta2) ||
+        !finite(hp->adam_eps) || !finite(hp->adam_weight_decay) || hp->adam_step < 1)
+      return MUON_E_ARG;
+    if (hp->adam_beta1 >= 1.f || hp->adam_beta2 >= 1.f) return MUON_E_ARG;
+  }
+  // pointer checks
+  for (int32_t p = 0; p < n; ++p) {
+    const muon_param_shape& s = P.table[p];
+    if (s.rows == 0 || s.cols == 0) continue;
+    const muon_param_ptrs& q = ptrs[p];
+    const size_t es = s.dtype == MUON_F32 ? 4 : 2;
+    if (!q.param || !q.grad || !aligned(q.param, es) || !aligned(q.grad, es)) return MUON_E_ARG;
+    if (s.kind == MUON_KIND_MUON) {
+      if (!q.momentum || !aligned(q.momentum, 4)) return MUON_E_ARG;
+      if (q.update_out && !aligned(q.update_out, 4)) return MUON_E_ARG;
+    } else {
+      if (!q.exp_avg || !q.exp_avg_sq || !aligned(q.exp_avg, 4) || !aligned(q.exp_avg_sq, 4))
+        return MUON_E_ARG;
+    }
+  }
+  if (P.lay.total > 0 && (!workspace || workspace_bytes < P.lay.total)) return MUON_E_WORKSPACE;
+  if (P.lay.total == 0) return MUON_OK;
+  hipStream_t st_ = reinterpret_cast<hipStream_t>(stream);
+  char* ws = align_base(workspace);
+
+  // per-unit descriptors, uploaded once per step
+  std::vector<UnitDesc> hd(P.units.size());
+  for (size_t i = 0; i < P.units.size(); ++i) {
+    const PlanUnit& u = P.units[i];
+    const muon_param_shape& s = P.table[u.param];
+    const muon_param_ptrs& q = ptrs[u.param];
+    const size_t es = s.dtype == MUON_F32 ? 4 : 2;
+    const int64_t off = u.row0 * s.cols;
+    UnitDesc d;
+    std::memset(&d, 0, sizeof(d));
+    d.g = static_cast<const char*>(q.grad) + off * es;
+    d.mom = q.momentum + off;
+    d.w = static_cast<char*>(q.param) + off * es;
+    d.o = q.update_out ? q.update_out + off : nullptr;
+    d.ld = s.cols;
+    d.scale = (float)((double)hp->rms_scale * std::sqrt((double)u.scale_dim));
+    hd[i] = d;
+  }
+  std::vector<AdamDesc> ad;
+  int64_t adam_blocks = 0;
+  for (int32_t p : P.adam) {
+    const muon_param_shape& s = P.table[p];
+    const int64_t numel = s.rows * s.cols;
+    if (numel == 0) continue;
+    const muon_param_ptrs& q = ptrs[p];
+    AdamDesc d;
+    std::memset(&d, 0, sizeof(d));
+    d.w = q.param;
+    d.g = q.grad;
+    d.m = q.exp_avg;
+    d.v = q.exp_avg_sq;
+    d.numel = numel;
+    d.block0 = adam_blocks;
+    d.dtype = dt_dev(s.dtype);
+    d.vec_ok = aligned(q.param, 16) && aligned(q.grad, 16) && aligned(q.exp_avg, 16) &&
+               aligned(q.exp_avg_sq, 16);
+    adam_blocks += ceil_div(numel, ADAM_EPB);
+    ad.push_back(d);
+  }
+  UnitDesc* d_desc = reinterpret_cast<UnitDesc*>(ws + P.lay.off_desc);
+  AdamDesc* d_adesc = reinterpret_cast<AdamDesc*>(ws + P.lay.off_adesc);
+  if (!hd.empty())
+    HIP_TRY(hipMemcpyAsync(d_desc, hd.data(), hd.size() * sizeof(UnitDesc), hipMemcpyHostToDevice, st_));
+  if (!ad.empty())
+    HIP_TRY(hipMemcpyAsync(d_adesc, ad.data(), ad.size() * sizeof(AdamDesc), hipMemcpyHostToDevice, st_));
+
+  ChainParams cp;
+  cp.mu = hp->momentum;
+  cp.nesterov = hp->nesterov ? 1 : 0;
+  cp.steps = hp->ns_steps;
+  cp.coeffs = coeffs.data();
+  cp.lr = hp->lr;
+  cp.wd = hp->weight_decay;
+  cp.final_mode = FINAL_UPDATE;
+  float4* d_aux = reinterpret_cast<float4*>(ws + P.lay.off_aux);
+  float* d_part = reinterpret_cast<float*>(ws + P.lay.off_part);
+  char* data = ws + P.lay.off_data;
+  for (const PlanBucket& b : P.buckets) {
+    for (int32_t s0 = 0; s0 < b.count; s0 += b.chunk) {
+      const int32_t cnt = std::min(b.chunk, b.count - s0);
+      bool vec = true;
+      for (int32_t i = 0; i < cnt && vec; ++i) {
+        const UnitDesc& d = hd[(size_t)b.first + s0 + i];
+        vec = aligned(d.g, 16) && aligned(d.mom, 16) && (d.ld % 8 == 0);
+      }
+      cp.vec_ok = vec ? 1 : 0;
+      st = run_chunk(b, d_desc + b.first + s0, d_aux, d_part, data, cnt, cp, st_);
+      if (st != MUON_OK) return st;
+    }
+  }
+  if (adam_blocks > 0) {
+    AdamArgs aa;
+    std::memset(&aa, 0, sizeof(aa));
+    aa.desc = d_adesc;
+    aa.nparams = (int32_t)ad.size();
+    aa.one_minus_b1 = 1.f - hp->adam_beta1;
+    aa.one_minus_b2 = 1.f - hp->adam_beta2;
+    aa.eps = hp->adam_eps;
+    aa.keep = 1.f - hp->adam_lr * hp->adam_weight_decay;
+    const double t = (double)hp->adam_step;
+    const double bc1 = 1.0 - std::pow((double)hp->adam_beta1, t);
+    const double bc2 = 1.0 - std::pow((double)hp->adam_beta2, t);
+    aa.step = (float)((double)hp->adam_lr * std::sqrt(bc2) / bc1);
+    HIP_TRY(launch_adamw(aa, adam_blocks, st_));
+  }
+  return MUON_OK;
+}
+
+static void ns_layout(const PlanBucket& b, size_t& off_aux, size_t& off_part, size_t& off_data,
+                      size_t& total) {
+  auto al = [](size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; };
+  off_aux = al(sizeof(UnitDesc));
+  off_part = off_aux + al(16);
+  off_data = off_part + al((size_t)b.km_tiles * 4);
+  total = off_data + b.data_bytes + WS_ALIGN;
+}
+
+static muon_status ns_bucket(int64_t rows, int64_t cols, int32_t dtype, int32_t method, PlanBucket& b) {
+  if (dtype != MUON_F32 && dtype != MUON_BF16) return MUON_E_DTYPE;
+  if (method != MUON_NS_STANDARD && method != MUON_NS_GRAM) return MUON_E_METHOD;
+  if (rows < 0 || cols < 0 || rows > ((int64_t)1 << 30) || cols > ((int64_t)1 << 30)) return MUON_E_SHAPE;
+  std::memset(&b, 0, sizeof(b));
+  b.m = (int32_t)std::min(rows, cols);
+  b.n = (int32_t)std::max(rows, cols);
+  b.tall = rows > cols ? 1 : 0;
+  b.pdtype = dtype;
+  b.cdtype = dtype;
+  b.method = method;
+  b.first = 0;
+  b.count = 1;
+  bucket_derive(b, ~size_t(0));
+  return MUON_OK;
+}
+
+muon_status ns_orthogonalize_workspace_bytes(int64_t rows, int64_t cols, int32_t dtype, int32_t method,
+                                             size_t* bytes) {
+  if (!bytes) return MUON_E_ARG;
+  PlanBucket b;
+  const muon_status st = ns_bucket(rows, cols, dtype, method, b);
+  if (st != MUON_OK) return st;
+  if (rows == 0 || cols == 0) {
+    *bytes = 0;
+    return MUON_OK;
+  }
+  size_t a, p, d, t;
+  ns_layout(b, a, p, d, t);
+  *bytes = t;
+  return MUON_OK;
+}
+
+muon_status ns_orthogonalize(void* X, int64_t rows, int64_t cols, int64_t ld, int32_t dtype, int32_t steps,
+                             const float* coeffs, int32_t method, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  PlanBucket b;
+  muon_status st = ns_bucket(rows, cols, dtype, method, b);
+  if (st != MUON_OK) return st;
+  std::vector<float> cf;
+  st = coeff_table(steps, coeffs, cf);
+  if (st != MUON_OK) return st;
+  if (ld < cols) return MUON_E_SHAPE;
+  if (rows == 0 || cols == 0) return MUON_OK;
+  const size_t es = dtype == MUON_F32 ? 4 : 2;
+  if (!X || !aligned(X, es)) return MUON_E_ARG;
+  size_t off_aux, off_part, off_data, total;
+  ns_layout(b, off_aux, off_part, off_data, total);
+  if (!workspace || workspace_bytes < total) return MUON_E_WORKSPACE;
+  hipStream_t st_ = reinterpret_cast<hipStream_t>(stream);
+  char* ws = align_base(workspace);
+  UnitDesc d;
+  std::memset(&d, 0, sizeof(d));
+  d.g = X;
+  d.mom = nullptr;
+  d.w = X;
+  d.o = nullptr;
+  d.ld = ld;
+  d.scale = 0.f;
+  HIP_TRY(hipMemcpyAsync(ws, &d, sizeof(d), hipMemcpyHostToDevice, st_));
+  ChainParams cp;
+  cp.mu = 0.f;
+  cp.nesterov = 0;
+  cp.steps = steps;
+  cp.coeffs = cf.data();
+  cp.lr = 0.f;
+  cp.wd = 0.f;
+  cp.final_mode = FINAL_STORE;
+  cp.vec_ok = aligned(X, 16) && (ld % 8 == 0);
+  return run_chunk(b, reinterpret_cast<UnitDesc*>(ws), reinterpret_cast<float4*>(ws + off_aux),
+                   reinterpret_cast<float*>(ws + off_part), ws + off_data, 1, cp, st_);
+}
+
+}  // extern "C"

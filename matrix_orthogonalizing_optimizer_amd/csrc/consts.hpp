@@ -1,0 +1,8 @@
+// Tiling constants shared by the host planner and the kernels.
+#pragma once
+
+namespace muon {
+constexpr int KM_TR = 32;       // momentum kernel tile rows (parameter layout)
+constexpr int KM_TC = 128;      // momentum kernel tile columns
+constexpr int ADAM_EPB = 4096;  // AdamW elements per workgroup
+}  // namespace muon

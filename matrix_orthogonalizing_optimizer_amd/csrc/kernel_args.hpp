@@ -1,0 +1,53 @@
+// Argument blocks of the libmuon kernels (shared by launchers and kernels).
+#pragma once
+
+#include "device_common.hpp"
+
+namespace muon {
+
+enum : int32_t { EPI_SCALE = 0, EPI_POLY = 1, EPI_AXPY = 2, EPI_FINAL = 3 };
+enum : int32_t { SEL_ONE = 0, SEL_INV_S = 1, SEL_INV_S2 = 2 };
+enum : int32_t { FINAL_UPDATE = 0, FINAL_STORE = 1 };
+
+struct GemmArgs {
+  const void* L;
+  const void* R;
+  const void* E;   // epilogue addend (EPI_POLY, EPI_AXPY, EPI_FINAL), same shape as C
+  void* C;
+  int64_t ldl, ldr, lde, ldc;
+  int64_t sL, sR, sE, sC;  // per-unit strides in elements
+  int32_t M, N, K;         // logical per-unit sizes
+  int32_t units, tilesM, tilesN, tilesPerUnit, totalTiles;
+  float alpha, beta, gamma;
+  int32_t alphaSel;        // SEL_*: alpha is multiplied by aux[u].y or aux[u].z
+  const float4* aux;       // per unit {s^2, 1/s, 1/s^2, 0}
+  const UnitDesc* desc;    // EPI_FINAL: per-unit parameter pointers
+  float lr, wd;            // EPI_FINAL
+  int32_t finalMode;       // FINAL_UPDATE or FINAL_STORE
+  int32_t tall;            // EPI_FINAL: the unit is the transpose of the parameter block
+  int32_t wdtype;          // EPI_FINAL: DT_F32 or DT_BF16
+};
+
+// Momentum kernel (see elementwise.hpp).
+struct MomArgs {
+  const UnitDesc* desc;
+  void* X0;
+  int64_t ldx;     // leading dimension of X0 (multiple of 8)
+  int64_t sX;      // per-unit element stride of X0
+  float* partials; // one per workgroup
+  int32_t rows, cols;      // unit shape in parameter layout
+  int32_t tilesR, tilesC, tilesPerUnit;
+  float mu;
+  int32_t nesterov;
+  int32_t vec_ok;  // every unit's g/mom rows are 16-byte aligned and cols % 8 == 0
+};
+
+// AdamW kernel (see elementwise.hpp).
+struct AdamArgs {
+  const AdamDesc* desc;
+  int64_t block_base;  // first global block of this launch
+  int32_t nparams;
+  float one_minus_b1, one_minus_b2, eps, keep, step;
+};
+
+}  // namespace muon

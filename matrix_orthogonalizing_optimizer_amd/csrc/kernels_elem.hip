@@ -1,0 +1,60 @@
+// Launchers of the elementwise kernels and the GEMM dtype dispatch.
+#include "elementwise.hpp"
+#include "launch.hpp"
+
+namespace muon {
+
+hipError_t launch_gemm(int tile, int ti, int to, bool rn, bool sym, int epi, const GemmArgs& a,
+                       hipStream_t s) {
+  if (a.totalTiles <= 0) return hipSuccess;
+  switch (ti) {
+    case DT_BF16: return launch_gemm_bf16(tile, to, rn, sym, epi, a, s);
+    case DT_F16: return launch_gemm_f16(tile, to, rn, sym, epi, a, s);
+    case DT_F32: return launch_gemm_f32(tile, to, rn, sym, epi, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_momentum(int gdtype, int xdtype, bool tall, const MomArgs& a, int64_t blocks,
+                           hipStream_t s) {
+  if (blocks <= 0) return hipSuccess;
+  const dim3 g((unsigned)blocks), b(256);
+  if (gdtype == DT_BF16 && xdtype == DT_BF16) {
+    if (tall) hipLaunchKernelGGL((momentum_kernel<bf16, bf16, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((momentum_kernel<bf16, bf16, false>), g, b, 0, s, a);
+  } else if (gdtype == DT_F32 && xdtype == DT_F32) {
+    if (tall) hipLaunchKernelGGL((momentum_kernel<float, float, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((momentum_kernel<float, float, false>), g, b, 0, s, a);
+  } else if (gdtype == DT_BF16 && xdtype == DT_F32) {
+    if (tall) hipLaunchKernelGGL((momentum_kernel<bf16, float, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((momentum_kernel<bf16, float, false>), g, b, 0, s, a);
+  } else if (gdtype == DT_F32 && xdtype == DT_BF16) {
+    if (tall) hipLaunchKernelGGL((momentum_kernel<float, bf16, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((momentum_kernel<float, bf16, false>), g, b, 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_finalize(const float* partials, int32_t per_unit, float4* aux, int32_t units,
+                                hipStream_t s) {
+  if (units <= 0) return hipSuccess;
+  hipLaunchKernelGGL(norm_finalize_kernel, dim3(units), dim3(256), 0, s, partials, per_unit, aux);
+  return hipGetLastError();
+}
+
+hipError_t launch_adamw(const AdamArgs& a0, int64_t total_blocks, hipStream_t s) {
+  const int64_t kMaxGrid = (int64_t)1 << 22;
+  AdamArgs a = a0;
+  for (int64_t b0 = 0; b0 < total_blocks; b0 += kMaxGrid) {
+    const int64_t nb = total_blocks - b0 < kMaxGrid ? total_blocks - b0 : kMaxGrid;
+    a.block_base = b0;
+    hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)nb), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace muon

@@ -1,0 +1,28 @@
+// Host-side launchers of the libmuon kernels (implemented in the .hip files).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "kernel_args.hpp"
+
+namespace muon {
+
+// GEMM launch for input dtype ti / output dtype to (DT_*), tile edge 128 or
+// 256, RN/RT operand layout, symmetric-output flag and epilogue kind.
+// Returns hipErrorInvalidValue for a combination that is not instantiated.
+hipError_t launch_gemm(int tile, int ti, int to, bool rn, bool sym, int epi, const GemmArgs& a,
+                       hipStream_t s);
+hipError_t launch_gemm_bf16(int tile, int to, bool rn, bool sym, int epi, const GemmArgs& a,
+                            hipStream_t s);
+hipError_t launch_gemm_f16(int tile, int to, bool rn, bool sym, int epi, const GemmArgs& a,
+                           hipStream_t s);
+hipError_t launch_gemm_f32(int tile, int to, bool rn, bool sym, int epi, const GemmArgs& a,
+                           hipStream_t s);
+
+hipError_t launch_momentum(int gdtype, int xdtype, bool tall, const MomArgs& a, int64_t blocks,
+                           hipStream_t s);
+hipError_t launch_norm_finalize(const float* partials, int32_t per_unit, float4* aux, int32_t units,
+                                hipStream_t s);
+hipError_t launch_adamw(const AdamArgs& a, int64_t total_blocks, hipStream_t s);
+
+}  // namespace muon

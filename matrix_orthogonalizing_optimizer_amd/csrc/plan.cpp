@@ -1,0 +1,151 @@
+// Host-only planner of libmuon (no HIP calls).
+//
+// A Muon parameter becomes one unit, or one unit per row block when
+// split_rows > 0 (the MindSpeed "Muon 优化器" document splits a fused QKV
+// weight into its Q/K/V sub-matrices and orthogonalizes each; the DeepSpeed
+// page names per-attention-head "Muon Split").  Units of equal
+// (m, n, tall, param dtype, compute dtype, method) share a bucket, numbered
+// by first appearance, and are processed together by grouped launches.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <cmath>
+
+#include "consts.hpp"
+
+namespace muon {
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+int32_t elem_size(int32_t cdtype) { return cdtype == MUON_F32 ? 4 : 2; }
+
+static size_t align_ws(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
+
+size_t per_unit_data_bytes(const PlanBucket& b) {
+  const size_t es = (size_t)elem_size(b.cdtype);
+  const size_t xb = (size_t)b.m * (size_t)b.ldx * es;
+  const size_t sb = (size_t)b.m * (size_t)b.mp * es;  // m x m (fp16 or fp32 in Gram)
+  if (b.method == MUON_NS_GRAM) return xb + 5 * sb;
+  return 2 * xb + 2 * sb;
+}
+
+void bucket_derive(PlanBucket& b, size_t chunk_cap_bytes) {
+  b.ldx = round_up(b.n, 8);
+  b.mp = round_up(b.m, 8);
+  b.tile = b.m <= 192 ? 128 : 256;
+  // momentum kernel tiles over the unit in parameter layout
+  const int64_t prow = b.tall ? b.n : b.m, pcol = b.tall ? b.m : b.n;
+  b.km_tiles = (int32_t)(((prow + KM_TR - 1) / KM_TR) * ((pcol + KM_TC - 1) / KM_TC));
+  const size_t per = per_unit_data_bytes(b);
+  int64_t chunk = (int64_t)(chunk_cap_bytes / std::max<size_t>(per, 1));
+  chunk = std::max<int64_t>(1, std::min<int64_t>(chunk, b.count));
+  b.chunk = (int32_t)chunk;
+  const size_t es = (size_t)elem_size(b.cdtype);
+  const size_t xb = align_ws((size_t)chunk * b.m * b.ldx * es);
+  const size_t sb = align_ws((size_t)chunk * b.m * b.mp * es);
+  size_t o = 0;
+  if (b.method == MUON_NS_GRAM) {
+    b.off[0] = o; o += xb;
+    for (int i = 1; i < 6; ++i) { b.off[i] = o; o += sb; }
+  } else {
+    b.off[0] = o; o += xb;
+    b.off[1] = o; o += xb;
+    b.off[2] = o; o += sb;
+    b.off[3] = o; o += sb;
+    b.off[4] = b.off[5] = 0;
+  }
+  b.data_bytes = o;
+}
+
+muon_status build_plan(const muon_param_shape* table, int32_t n, const muon_plan_options* opts,
+                       PlanImpl& P) {
+  if (n < 0 || (n > 0 && !table)) return MUON_E_ARG;
+  muon_plan_options o{MUON_NS_STANDARD, -1};
+  if (opts) o = *opts;
+  if (o.ns_method != MUON_NS_STANDARD && o.ns_method != MUON_NS_GRAM) return MUON_E_METHOD;
+  if (o.ns_dtype != -1 && o.ns_dtype != MUON_F32 && o.ns_dtype != MUON_BF16) return MUON_E_DTYPE;
+  P.table.assign(table, table + n);
+  P.opts = o;
+  const int64_t kMaxDim = (int64_t)1 << 30;
+
+  std::vector<PlanUnit> order;  // table order
+  for (int32_t p = 0; p < n; ++p) {
+    const muon_param_shape& s = table[p];
+    if (s.kind != MUON_KIND_MUON && s.kind != MUON_KIND_ADAMW) return MUON_E_ARG;
+    if (s.dtype != MUON_F32 && s.dtype != MUON_BF16) return MUON_E_DTYPE;
+    if (s.rows < 0 || s.cols < 0 || s.split_rows < 0 || s.scale_dim < 0) return MUON_E_SHAPE;
+    if (s.rows > kMaxDim || s.cols > kMaxDim) return MUON_E_SHAPE;
+    if (s.kind == MUON_KIND_ADAMW) {
+      if (s.split_rows != 0) return MUON_E_SHAPE;
+      P.adam.push_back(p);
+      continue;
+    }
+    if (s.split_rows > 0 && s.rows % s.split_rows != 0) return MUON_E_SHAPE;
+    if (s.rows == 0 || s.cols == 0) continue;
+    const int64_t h = s.split_rows > 0 ? s.split_rows : s.rows;
+    for (int64_t r = 0; r < s.rows; r += h) {
+      PlanUnit u;
+      u.param = p;
+      u.row0 = r;
+      u.rows = h;
+      u.cols = s.cols;
+      u.tall = h > s.cols ? 1 : 0;
+      u.scale_dim = s.scale_dim > 0 ? s.scale_dim : std::max(h, s.cols);
+      order.push_back(u);
+    }
+  }
+
+  // buckets by first appearance
+  std::vector<std::vector<int32_t>> members;
+  for (size_t i = 0; i < order.size(); ++i) {
+    const PlanUnit& u = order[i];
+    const int32_t m = (int32_t)std::min(u.rows, u.cols), nn = (int32_t)std::max(u.rows, u.cols);
+    const int32_t pdt = P.table[u.param].dtype;
+    const int32_t cdt = o.ns_dtype < 0 ? pdt : o.ns_dtype;
+    size_t bi = 0;
+    for (; bi < P.buckets.size(); ++bi) {
+      const PlanBucket& b = P.buckets[bi];
+      if (b.m == m && b.n == nn && b.tall == u.tall && b.pdtype == pdt && b.cdtype == cdt) break;
+    }
+    if (bi == P.buckets.size()) {
+      PlanBucket b{};
+      b.m = m;
+      b.n = nn;
+      b.tall = u.tall;
+      b.pdtype = pdt;
+      b.cdtype = cdt;
+      b.method = o.ns_method;
+      P.buckets.push_back(b);
+      members.emplace_back();
+    }
+    members[bi].push_back((int32_t)i);
+  }
+  P.units.clear();
+  for (size_t bi = 0; bi < P.buckets.size(); ++bi) {
+    PlanBucket& b = P.buckets[bi];
+    b.first = (int32_t)P.units.size();
+    b.count = (int32_t)members[bi].size();
+    for (int32_t i : members[bi]) P.units.push_back(order[i]);
+    bucket_derive(b, CHUNK_CAP_BYTES);
+    P.max_chunk = std::max(P.max_chunk, b.chunk);
+    P.max_partials = std::max<int64_t>(P.max_partials, (int64_t)b.chunk * b.km_tiles);
+    P.max_data = std::max(P.max_data, b.data_bytes);
+  }
+
+  Layout& L = P.lay;
+  size_t off = 0;
+  L.off_desc = off;
+  off = align_ws(off + P.units.size() * 48);
+  L.off_adesc = off;
+  off = align_ws(off + P.adam.size() * 64);
+  L.off_aux = off;
+  off = align_ws(off + (size_t)P.max_chunk * 16);
+  L.off_part = off;
+  off = align_ws(off + (size_t)P.max_partials * 4);
+  L.off_data = off;
+  off += P.max_data;
+  L.total = off == 0 ? 0 : off + WS_ALIGN;  // slack to align the caller's base
+  return MUON_OK;
+}
+
+}  // namespace muon

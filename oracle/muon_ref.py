@@ -251,16 +251,18 @@ def plan_units(table) -> List[OracleUnit]:
 
 
 def plan_buckets(table, method: int, ns_dtype: int = -1):
-    """Group units with the same (m, n, tall, compute dtype, method).  Buckets
-    are numbered by first appearance; units inside a bucket keep table order.
-    Brute force: for every unit, scan the buckets seen so far.  ``ns_dtype``
-    -1 means the compute dtype follows the parameter dtype."""
+    """Group units with the same (m, n, tall, parameter dtype, compute dtype,
+    method).  Buckets are numbered by first appearance; units inside a bucket
+    keep table order.  Brute force: for every unit, scan the buckets seen so
+    far.  ``ns_dtype`` -1 means the compute dtype follows the parameter
+    dtype."""
     units = plan_units(table)
     keys = []
     members = []
     for ui, u in enumerate(units):
-        dt = table[u.param][1] if ns_dtype < 0 else ns_dtype
-        key = (u.m, u.n, 1 if u.tall else 0, dt, method)
+        pdt = table[u.param][1]
+        dt = pdt if ns_dtype < 0 else ns_dtype
+        key = (u.m, u.n, 1 if u.tall else 0, pdt, dt, method)
         found = -1
         for bi, k in enumerate(keys):
             if k == key:

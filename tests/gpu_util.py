@@ -1,0 +1,51 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C-ABI
+binding and bring results back as float64 numpy arrays for the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import matrix_orthogonalizing_optimizer_amd as mo
+
+
+def dev():
+    if not torch.cuda.is_available():
+        raise RuntimeError("no GPU visible: the gpu tests need an MI355X")
+    mo.lib()  # fail loudly when libmuon.so is missing
+    return torch.device("cuda:0")
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def rel(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def to_dev(x, dtype, device):
+    return torch.as_tensor(np.asarray(x)).to(device=device, dtype=dtype).contiguous()
+
+
+class StepRunner:
+    """Owns plan + workspace for one shape table and runs muon_step."""
+
+    def __init__(self, table, method=0, ns_dtype=-1, device=None):
+        self.device = device or dev()
+        self.table = table
+        self.plan = mo.muon_plan_create(table, method, ns_dtype)
+        nb = mo.muon_plan_workspace_bytes(self.plan)
+        self.ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=self.device)
+
+    def step(self, params, grads, moms, eas, ess, hp, update_outs=None):
+        mo.muon_step(self.plan, params, grads, moms, eas, ess, hp, self.ws, update_outs=update_outs)
+
+
+def hp_from(d: dict, adam_step: int = 1, coeffs=None):
+    return mo.make_hparams(lr=d["lr"], momentum=d["momentum"], weight_decay=d["weight_decay"],
+                           nesterov=d["nesterov"], ns_steps=d["ns_steps"], coeffs=coeffs,
+                           adam_lr=d["adam_lr"], adam_beta1=d["adam_beta1"],
+                           adam_beta2=d["adam_beta2"], adam_eps=d["adam_eps"],
+                           adam_weight_decay=d["adam_weight_decay"], adam_step=adam_step)

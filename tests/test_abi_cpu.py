@@ -1,0 +1,157 @@
+"""Host-side checks of libmuon that need no GPU: the library loads and
+exports every function include/libmuon.h declares, the planner matches the
+oracle's independent brute-force bucketing bit for bit, and invalid
+arguments are rejected before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from workloads import configs
+
+mo = pytest.importorskip("matrix_orthogonalizing_optimizer_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib_or_skip():
+    try:
+        return mo.lib()
+    except RuntimeError as e:  # not built in this checkout
+        pytest.skip(str(e))
+
+
+def declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for fn in sorted(os.listdir(inc)):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(inc, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                             text, flags=re.M):
+            names.append(m.group(1))
+    return names
+
+
+def test_exports_every_declared_function():
+    L = _lib_or_skip()
+    names = declared_functions()
+    assert set(names) >= {"muon_step", "ns_orthogonalize", "muon_plan_create"}
+    for n in names:
+        assert hasattr(L, n), f"libmuon.so does not export {n}"
+    assert sorted(names) == sorted(mo.EXPORTED)
+    assert mo.muon_version() >= 100
+    for code in range(-8, 1):
+        assert mo.muon_status_string(code) != "unknown status"
+
+
+@pytest.mark.parametrize("name", list(configs.ALL))
+@pytest.mark.parametrize("ns_dtype", [-1, 0])
+def test_plan_matches_oracle_bit_exact(name, ns_dtype):
+    _lib_or_skip()
+    wl = configs.ALL[name]()
+    method = 1 if wl.method == "gram" else 0
+    plan = mo.muon_plan_create(wl.table, method, ns_dtype)
+    units, keys, members = oracle.plan_buckets(wl.table, method, ns_dtype)
+    got_b = mo.muon_plan_buckets(plan)
+    exp_b, first = [], 0
+    for k, mem in zip(keys, members):
+        exp_b.append(tuple(k) + (first, len(mem)))
+        first += len(mem)
+    assert got_b == exp_b
+    exp_u = []
+    for mem in members:
+        for ui in mem:
+            u = units[ui]
+            exp_u.append((u.param, u.row0, u.rows, u.cols, int(u.tall),
+                          u.scale_dim if u.scale_dim > 0 else max(u.rows, u.cols)))
+    assert mo.muon_plan_units(plan) == exp_u
+    ws = mo.muon_plan_workspace_bytes(plan)
+    assert ws > 0
+
+
+def test_plan_mixed_and_edge_tables():
+    _lib_or_skip()
+    table = [(0, 1, 6, 4, 2, 0),      # 3 row blocks 2x4
+             (1, 1, 1, 7, 0, 0),      # vector -> AdamW
+             (0, 0, 5, 3, 0, 11),     # tall fp32 with a scale override
+             (0, 1, 0, 9, 0, 0),      # empty: no unit
+             (0, 1, 2, 4, 0, 0),      # same bucket as the blocks
+             (0, 0, 37, 50, 0, 0)]    # ragged
+    plan = mo.muon_plan_create(table)
+    units, keys, members = oracle.plan_buckets(table, 0)
+    assert [b[:6] for b in mo.muon_plan_buckets(plan)] == [tuple(k) for k in keys]
+    assert [b[7] for b in mo.muon_plan_buckets(plan)] == [len(m) for m in members]
+    assert mo.muon_plan_units(plan)[3] == (4, 0, 2, 4, 0, 4)
+    empty = mo.muon_plan_create([])
+    assert mo.muon_plan_buckets(empty) == [] and mo.muon_plan_workspace_bytes(empty) == 0
+
+
+@pytest.mark.parametrize("row,status", [
+    ((2, 1, 4, 4, 0, 0), -1),    # unknown kind
+    ((0, 5, 4, 4, 0, 0), -3),    # unknown dtype
+    ((0, 1, -1, 4, 0, 0), -2),   # negative rows
+    ((0, 1, 6, 4, 4, 0), -2),    # split does not divide rows
+    ((1, 1, 6, 4, 2, 0), -2),    # split on an AdamW row
+    ((0, 1, 4, 1 << 31, 0, 0), -2),  # side too large
+])
+def test_plan_rejects(row, status):
+    _lib_or_skip()
+    with pytest.raises(mo.MuonError) as e:
+        mo.muon_plan_create([row])
+    assert e.value.status == status
+    with pytest.raises(mo.MuonError) as e:
+        mo.muon_plan_create([(0, 1, 4, 4, 0, 0)], ns_method=7)
+    assert e.value.status == -4
+
+
+def test_step_validation_before_any_launch():
+    L = _lib_or_skip()
+    from matrix_orthogonalizing_optimizer_amd import _lib as B
+    plan = mo.muon_plan_create([(0, 1, 4, 8, 0, 0)])
+    hp = mo.make_hparams()
+    ptrs = (B.MuonParamPtrs * 1)()
+    ptrs[0] = B.MuonParamPtrs(0x1000, 0x2000, 0x3000, None, None, None)
+    ws = mo.muon_plan_workspace_bytes(plan)
+    # table size mismatch
+    assert L.muon_step(plan.handle, ptrs, 2, ctypes.byref(hp), 0x10000, ws, None) == -7
+    # null plan / hparams / pointer arrays
+    assert L.muon_step(None, ptrs, 1, ctypes.byref(hp), 0x10000, ws, None) == -1
+    assert L.muon_step(plan.handle, ptrs, 1, None, 0x10000, ws, None) == -1
+    assert L.muon_step(plan.handle, None, 1, ctypes.byref(hp), 0x10000, ws, None) == -1
+    # workspace too small / missing
+    assert L.muon_step(plan.handle, ptrs, 1, ctypes.byref(hp), 0x10000, ws - 1, None) == -5
+    assert L.muon_step(plan.handle, ptrs, 1, ctypes.byref(hp), None, ws, None) == -5
+    # misaligned bf16 param, missing momentum
+    ptrs[0] = B.MuonParamPtrs(0x1001, 0x2000, 0x3000, None, None, None)
+    assert L.muon_step(plan.handle, ptrs, 1, ctypes.byref(hp), 0x10000, ws, None) == -1
+    ptrs[0] = B.MuonParamPtrs(0x1000, 0x2000, None, None, None, None)
+    assert L.muon_step(plan.handle, ptrs, 1, ctypes.byref(hp), 0x10000, ws, None) == -1
+    # non-finite hyperparameter, bad step count, non-finite coefficient
+    ptrs[0] = B.MuonParamPtrs(0x1000, 0x2000, 0x3000, None, None, None)
+    bad = mo.make_hparams(lr=float("nan"))
+    assert L.muon_step(plan.handle, ptrs, 1, ctypes.byref(bad), 0x10000, ws, None) == -1
+    bad = mo.make_hparams(ns_steps=0)
+    assert L.muon_step(plan.handle, ptrs, 1, ctypes.byref(bad), 0x10000, ws, None) == -1
+    bad = mo.make_hparams(ns_steps=2, coeffs=[(1.0, float("inf"), 0.0), (1.0, 0.0, 0.0)])
+    assert L.muon_step(plan.handle, ptrs, 1, ctypes.byref(bad), 0x10000, ws, None) == -1
+
+
+def test_ns_orthogonalize_validation():
+    L = _lib_or_skip()
+    assert mo.ns_orthogonalize_workspace_bytes(0, 5, 1) == 0
+    nb = mo.ns_orthogonalize_workspace_bytes(64, 96, 1)
+    assert nb > 64 * 96 * 2 * 2
+    assert mo.ns_orthogonalize_workspace_bytes(96, 64, 1) == nb  # tall uses the same shape
+    f = L.ns_orthogonalize
+    assert f(0x1000, 64, 96, 96, 9, 5, None, 0, 0x10000, nb, None) == -3
+    assert f(0x1000, 64, 96, 96, 1, 5, None, 3, 0x10000, nb, None) == -4
+    assert f(0x1000, 64, 96, 90, 1, 5, None, 0, 0x10000, nb, None) == -2
+    assert f(0x1000, 64, 96, 96, 1, 0, None, 0, 0x10000, nb, None) == -1
+    assert f(None, 64, 96, 96, 1, 5, None, 0, 0x10000, nb, None) == -1
+    assert f(0x1000, 64, 96, 96, 1, 5, None, 0, 0x10000, nb - 1, None) == -5
+    assert f(0x1000, 0, 96, 96, 1, 5, None, 0, None, 0, None) == 0   # empty: nothing to do

@@ -1,0 +1,151 @@
+"""GPU parity of muon_step against the fp64 oracle on the small workloads:
+the single 256x512 fp32 matrix over three steps (fp32 path, 1e-4) and the
+GPT-2-small-shaped set (bf16 path, 2e-2; QKV split blocks, tall MLP-up,
+AdamW embedding and vectors).  Momentum and AdamW moments are compared at
+1e-6 relative; the orthogonalized update O of every checked unit is read
+back through update_out."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import StepRunner, dev, f64, hp_from, rel
+from workloads import configs, gen
+
+mo = pytest.importorskip("matrix_orthogonalizing_optimizer_amd")
+
+pytestmark = pytest.mark.gpu
+
+
+def _state(wl, device):
+    params, moms, eas, ess = gen.make_state(wl, "cpu")
+    to = lambda xs: [None if x is None else x.to(device) for x in xs]
+    return to(params), to(moms), to(eas), to(ess)
+
+
+def _oracle_hp(d, adam_step=1):
+    return oracle.OracleHparams(lr=d["lr"], momentum=d["momentum"], weight_decay=d["weight_decay"],
+                                nesterov=d["nesterov"], ns_steps=d["ns_steps"], adam_lr=d["adam_lr"],
+                                adam_beta1=d["adam_beta1"], adam_beta2=d["adam_beta2"],
+                                adam_eps=d["adam_eps"], adam_weight_decay=d["adam_weight_decay"],
+                                adam_step=adam_step)
+
+
+def test_single_fp32_three_steps():
+    print("muon_step single_256x512_fp32", flush=True)
+    d = dev()
+    wl = configs.single_256x512()
+    P, M, EA, ES = _state(wl, d)
+    run = StepRunner(wl.table, device=d)
+    W_ref = [f64(P[0])]
+    M_ref = [f64(M[0])]
+    for step in range(wl.steps):
+        G = gen.make_grads(wl, step, "cpu")
+        Gd = [g.to(d) for g in G]
+        O = torch.zeros(256, 512, dtype=torch.float32, device=d)
+        W_old = f64(P[0])
+        run.step(P, Gd, M, EA, ES, hp_from(wl.hp), update_outs=[O])
+        torch.cuda.synchronize()
+        out = oracle.muon_step(wl.table, W_ref, [f64(G[0])], M_ref, [None], [None], _oracle_hp(wl.hp),
+                               want_updates=True)
+        W_ref, M_ref = out["W"], out["M"]
+        assert rel(f64(O), out["O"][0]) <= 1e-4
+        assert rel(f64(M[0]), M_ref[0]) <= 1e-6
+        assert rel(f64(P[0]) - W_old, W_ref[0] - W_old) <= 1e-4
+        assert rel(f64(P[0]), W_ref[0]) <= 1e-6
+
+
+def test_gpt2_small_bf16_sampled():
+    print("muon_step gpt2_small_bf16", flush=True)
+    d = dev()
+    wl = configs.gpt2_small()
+    P, M, EA, ES = _state(wl, d)
+    G = gen.make_grads(wl, 0, "cpu")
+    Gd = [g.to(d) for g in G]
+    outs = [torch.zeros(r[2], r[3], dtype=torch.float32, device=d) if r[0] == 0 else None
+            for r in wl.table]
+    W0 = [f64(p) for p in P]
+    run = StepRunner(wl.table, device=d)
+    run.step(P, Gd, M, EA, ES, hp_from(wl.hp), update_outs=outs)
+    torch.cuda.synchronize()
+    # oracle on layers 0 and 11 (qkv blocks, attn-out, tall mlp-up, mlp-down)
+    units = oracle.plan_units(wl.table)
+    sel = [i for i, u in enumerate(units) if u.param < 4 or 44 <= u.param < 48]
+    Wg = [f64(p) if r[0] == 0 else None for p, r in zip(P, wl.table)]
+    zeros_muon = [np.zeros((r[2], r[3])) if r[0] == 0 else None for r in wl.table]
+    ref = oracle.muon_step(wl.table, W0, [f64(g) for g in G], zeros_muon,
+                           [np.zeros((r[2], r[3])) if r[0] == 1 else None for r in wl.table],
+                           [np.zeros((r[2], r[3])) if r[0] == 1 else None for r in wl.table],
+                           _oracle_hp(wl.hp), units_subset=sel, want_updates=True)
+    worst = 0.0
+    for ui in sel:
+        u = units[ui]
+        r0, r1 = u.row0, u.row0 + u.rows
+        o = f64(outs[u.param])[r0:r1]
+        e = rel(o, ref["O"][ui])
+        worst = max(worst, e)
+        assert e <= 2e-2, (ui, e)
+        dw = Wg[u.param][r0:r1] - W0[u.param][r0:r1]
+        dw_ref = ref["W"][u.param][r0:r1] - W0[u.param][r0:r1]
+        assert rel(dw, dw_ref) <= 2e-2, (ui, rel(dw, dw_ref))
+        assert rel(f64(M[u.param])[r0:r1], ref["M"][u.param][r0:r1]) <= 1e-6
+    print("worst unit O rel err", worst)
+    # AdamW: every element of the embedding and vectors
+    for p, r in enumerate(wl.table):
+        if r[0] != 1:
+            continue
+        assert rel(f64(EA[p]), ref["exp_avg"][p]) <= 1e-6
+        assert rel(f64(ES[p]), ref["exp_avg_sq"][p]) <= 1e-6
+        assert rel(f64(P[p]) - W0[p], ref["W"][p] - W0[p]) <= 2e-2
+
+
+def test_grouped_equals_single_and_resume():
+    """A unit computed inside a grouped launch is bit-identical to the same
+    unit planned alone; two steps equal one step, copy of state, one step."""
+    d = dev()
+    table = [(0, 1, 384, 640, 0, 0)] * 5
+    wl = configs.Workload("five", table, [f"w{i}" for i in range(5)], rank=8, hp=configs._hp())
+    P, M, EA, ES = _state(wl, d)
+    G = [g.to(d) for g in gen.make_grads(wl, 0, "cpu")]
+    outs = [torch.zeros(384, 640, dtype=torch.float32, device=d) for _ in range(5)]
+    StepRunner(table, device=d).step([p.clone() for p in P], G, [m.clone() for m in M], EA, ES,
+                                     hp_from(wl.hp), update_outs=outs)
+    one = StepRunner(table[:1], device=d)
+    for i in range(5):
+        o = torch.zeros(384, 640, dtype=torch.float32, device=d)
+        one.step([P[i].clone()], [G[i]], [M[i].clone()], [None], [None], hp_from(wl.hp), update_outs=[o])
+        torch.cuda.synchronize()
+        assert torch.equal(o, outs[i])
+    # resume: state copied between steps gives the identical trajectory
+    run = StepRunner(table, device=d)
+    Pa, Ma = [p.clone() for p in P], [m.clone() for m in M]
+    Pb, Mb = [p.clone() for p in P], [m.clone() for m in M]
+    G2 = [g.to(d) for g in gen.make_grads(wl, 1, "cpu")]
+    run.step(Pa, G, Ma, EA, ES, hp_from(wl.hp))
+    run.step(Pa, G2, Ma, EA, ES, hp_from(wl.hp))
+    run.step(Pb, G, Mb, EA, ES, hp_from(wl.hp))
+    Pc = [p.cpu().clone().to(d) for p in Pb]
+    Mc = [m.cpu().clone().to(d) for m in Mb]
+    StepRunner(table, device=d).step(Pc, G2, Mc, EA, ES, hp_from(wl.hp))
+    torch.cuda.synchronize()
+    for a, b in zip(Pa, Pc):
+        assert torch.equal(a, b)
+    for a, b in zip(Ma, Mc):
+        assert torch.equal(a, b)
+
+
+def test_non_nesterov_and_zero_gradient_unit():
+    d = dev()
+    table = [(0, 0, 96, 160, 0, 0), (0, 0, 64, 64, 0, 0)]
+    wl = configs.Workload("nn", table, ["a", "z"], rank=4, hp=configs._hp(nesterov=False))
+    P, M, EA, ES = _state(wl, d)
+    G = gen.make_grads(wl, 0, "cpu")
+    G[1] = torch.zeros_like(G[1])
+    W0 = [f64(p) for p in P]
+    StepRunner(table, device=d).step(P, [g.to(d) for g in G], M, EA, ES, hp_from(wl.hp))
+    torch.cuda.synchronize()
+    ref = oracle.muon_step(table, W0, [f64(g) for g in G], [np.zeros((96, 160)), np.zeros((64, 64))],
+                           [None, None], [None, None], _oracle_hp(wl.hp))
+    assert rel(f64(P[0]) - W0[0], ref["W"][0] - W0[0]) <= 1e-4
+    # zero gradient: O = 0, the weight only decays
+    assert rel(f64(P[1]), W0[1] * (1 - wl.hp["lr"] * wl.hp["weight_decay"])) <= 1e-6

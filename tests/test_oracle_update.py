@@ -114,7 +114,7 @@ def _bucket_summary(table, method=0):
 def test_plan_gpt2():
     summ, units, members = _bucket_summary(configs.gpt2_small().table)
     assert len(units) == 12 * 6
-    assert summ == [((768, 768, 0, 1, 0), 48), ((768, 3072, 1, 1, 0), 12), ((768, 3072, 0, 1, 0), 12)]
+    assert summ == [((768, 768, 0, 1, 1, 0), 48), ((768, 3072, 1, 1, 1, 0), 12), ((768, 3072, 0, 1, 1, 0), 12)]
     # units keep table order inside a bucket
     for mem in members:
         assert mem == sorted(mem)
@@ -123,11 +123,11 @@ def test_plan_gpt2():
 
 def test_plan_llama_and_moe():
     summ, _, _ = _bucket_summary(configs.llama3_8b().table)
-    assert summ == [((4096, 4096, 0, 1, 0), 64), ((1024, 4096, 0, 1, 0), 64),
-                    ((4096, 14336, 1, 1, 0), 64), ((4096, 14336, 0, 1, 0), 32)]
+    assert summ == [((4096, 4096, 0, 1, 1, 0), 64), ((1024, 4096, 0, 1, 1, 0), 64),
+                    ((4096, 14336, 1, 1, 1, 0), 64), ((4096, 14336, 0, 1, 1, 0), 32)]
     summ, units, _ = _bucket_summary(configs.moe_grouped().table)
     assert len(units) == 6656
-    assert summ == [((128, 2048, 0, 1, 0), 1664), ((1408, 2048, 0, 1, 0), 3328),
-                    ((1408, 2048, 1, 1, 0), 1664)]
+    assert summ == [((128, 2048, 0, 1, 1, 0), 1664), ((1408, 2048, 0, 1, 1, 0), 3328),
+                    ((1408, 2048, 1, 1, 1, 0), 1664)]
     summ, _, _ = _bucket_summary(configs.wide_gram().table, 1)
-    assert summ == [((4096, 14336, 0, 1, 1), 32), ((4096, 14336, 1, 1, 1), 32)]
+    assert summ == [((4096, 14336, 0, 1, 1, 1), 32), ((4096, 14336, 1, 1, 1, 1), 32)]
