@@ -1,0 +1,196 @@
+"""Benchmark of one Muon optimizer step on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Default workload: the Llama-3-8B-shaped weight set (32 layers x {q, k, v, o,
+gate, up, down} in bf16 with fp32 momentum, Newton-Schulz standard method,
+five quintic steps, plus AdamW on the 128256 x 4096 embedding and lm_head and
+65 RMSNorm vectors).  Inputs are synthetic and already resident in HBM when
+the timed region starts: rank-64 geometric-spectrum gradients plus noise,
+generated on the GPU from seeded torch generators.
+
+Prints one JSON line: value = nominal Newton-Schulz TFLOP/s of the whole step
+(5 x sum over units of 4 m^2 n + 2 m^3, m <= n, divided by the step time),
+ms_per_step, the roofline of the dominant kernel (the B X update GEMM,
+timed live with HIP events around each of its launches) and the fp64 oracle
+timed on the host cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="llama3_8b_bf16")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample", default="1024x4096,4096x4096",
+                   help="unit shapes the oracle is timed on")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
+              "owner-computes step is a design, not built", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import matrix_orthogonalizing_optimizer_amd as mo
+    from workloads import configs, gen
+
+    mo.lib()
+    dev = torch.device("cuda:0")
+    wl = configs.ALL[args.workload]()
+    method = 1 if wl.method == "gram" else 0
+    table = wl.table
+
+    # ---- inputs (untimed), resident in HBM
+    t0 = time.time()
+    params, grads, moms, eas, ess = [], [], [], [], []
+    for p, (kind, dt, rows, cols, _s, _sd) in enumerate(table):
+        tdt = gen.torch_dtype(dt)
+        params.append(gen.normal(rows, cols, gen.W_STD, gen.stream_seed(0, 4, p, 1 << 20), dev, tdt))
+        if kind == 0:
+            grads.append(gen.lowrank_gradient(rows, cols, wl.rank, gen.stream_seed(0, 4, p, 0), dev, tdt))
+            moms.append(torch.zeros(rows, cols, dtype=torch.float32, device=dev))
+            eas.append(None)
+            ess.append(None)
+        else:
+            grads.append(gen.normal(rows, cols, gen.ADAM_G_STD, gen.stream_seed(0, 4, p, 0), dev, tdt))
+            moms.append(None)
+            eas.append(torch.zeros(rows, cols, dtype=torch.float32, device=dev))
+            ess.append(torch.zeros(rows, cols, dtype=torch.float32, device=dev))
+    plan = mo.muon_plan_create(table, method)
+    ws = torch.empty(mo.muon_plan_workspace_bytes(plan), dtype=torch.uint8, device=dev)
+    hp = mo.make_hparams(**{k: v for k, v in wl.hp.items()})
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.time() - t0:.1f} s; workspace {ws.numel() / 2**30:.2f} GiB",
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        mo.muon_step(plan, params, grads, moms, eas, ess, hp, ws, stream=stream)
+    torch.cuda.synchronize()
+    print("# warmup done", file=sys.stderr, flush=True)
+
+    # ---- timed region: K whole steps, kernel launches bracketed by HIP events
+    mo.muon_timing_enable(True)
+    mo.muon_timing_collect()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        mo.muon_step(plan, params, grads, moms, eas, ess, hp, ws, stream=stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    mo.muon_timing_enable(False)
+    kt = mo.muon_timing_collect()
+    ms_per_step = 1e3 * elapsed / args.steps
+    print(f"# timed {args.steps} steps: {ms_per_step:.2f} ms/step", file=sys.stderr, flush=True)
+
+    ns_flops = wl.hp["ns_steps"] * configs.ns_flops(table)
+    tflops = ns_flops / (ms_per_step * 1e-3) / 1e12
+
+    kernels = {}
+    for name, r in kt.items():
+        avg = r["total_ms"] / max(r["launches"], 1)
+        e = {"launches": r["launches"] // args.steps, "ms_per_step": r["total_ms"] / args.steps,
+             "avg_launch_ms": avg}
+        if r["flops"] > 0:
+            e["tflops"] = r["flops"] / (r["total_ms"] * 1e-3) / 1e12
+        if r["bytes"] > 0:
+            e["gbs"] = r["bytes"] / (r["total_ms"] * 1e-3) / 1e9
+        kernels[name] = e
+    dom = "ns_update_aX_BX" if "ns_update_aX_BX" in kt else max(kt, key=lambda k: kt[k]["total_ms"])
+    d = kt[dom]
+    achieved = d["flops"] / d["launches"] / (d["total_ms"] / d["launches"] * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
+                "flops_per_launch": d["flops"] / d["launches"],
+                "avg_launch_ms": d["total_ms"] / d["launches"], "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.cpu_sample, wl, table)
+
+    n_units = len(mo.muon_plan_units(plan))
+    adam_elems = sum(r[2] * r[3] for r in table if r[0] == 1)
+    muon_elems = sum(r[2] * r[3] for r in table if r[0] == 0)
+    out = {
+        "metric": "Muon step ms + NS TFLOP/s (% bf16 MFMA peak), 8B-shaped weight set, 1 GPU",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if table[0][1] == 1 else "f32",
+        "data": "synthetic",
+        "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
+        "config": {"workload": wl.name, "units": n_units, "buckets": len(mo.muon_plan_buckets(plan)),
+                   "ns_steps": wl.hp["ns_steps"], "ns_method": wl.method,
+                   "muon_elements": muon_elems, "adamw_elements": adam_elems,
+                   "ns_nominal_tflop_per_step": ns_flops / 1e12},
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(sample: str, wl, table):
+    """The fp64 oracle as it stands, timed on this host on a bounded sample:
+    one full Muon unit update (momentum, Newton-Schulz, scaled update) per
+    listed unit shape, with the workload's gradient generator.  Reported as
+    nominal Newton-Schulz TFLOP/s, the metric's unit."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from workloads import gen
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = os.cpu_count() or 1
+    flops = 0.0
+    secs = 0.0
+    shapes = []
+    for s in sample.split(","):
+        r, c = (int(x) for x in s.split("x"))
+        G = gen.lowrank_gradient(r, c, wl.rank, 99, "cpu", torch.float64).to(torch.bfloat16).double().numpy()
+        W = np.zeros((r, c))
+        hp = oracle.OracleHparams(**{k: v for k, v in wl.hp.items() if k in oracle.OracleHparams.__annotations__})
+        t = time.perf_counter()
+        oracle.muon_step([(0, 1, r, c, 0, 0)], [W], [G], [np.zeros((r, c))], [None], [None], hp)
+        secs += time.perf_counter() - t
+        m, n = min(r, c), max(r, c)
+        flops += wl.hp["ns_steps"] * (4.0 * m * m * n + 2.0 * m ** 3)
+        shapes.append(f"{r}x{c}")
+    rate = flops / secs / 1e12
+    step_flops = wl.hp["ns_steps"] * __import__("workloads").configs.ns_flops(table)
+    return {"value": rate, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"one Muon unit update per shape {','.join(shapes)} of the workload "
+                      f"({flops / 1e12:.2f} TFLOP nominal, {secs:.1f} s)",
+            "extrapolated_ms_per_step": 1e3 * step_flops / (rate * 1e12)}
+
+
+if __name__ == "__main__":
+    main()

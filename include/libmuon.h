@@ -176,6 +176,29 @@ muon_status ns_orthogonalize(void* X, int64_t rows, int64_t cols, int64_t ld, in
 muon_status ns_orthogonalize_workspace_bytes(int64_t rows, int64_t cols, int32_t dtype,
                                              int32_t method, size_t* bytes);
 
+/* Optional per-kernel timing, for benchmarks.  While enabled (process-wide),
+ * every kernel launch of the library is bracketed by two HIP events recorded
+ * on the launch's stream, tagged with the kernel family and the algorithmic
+ * FLOPs / HBM bytes of that launch:
+ *   flops  Newton-Schulz contractions: 2*m*m*n (X X^T and B X) or 2*m^3
+ *          (A A and the Gram m x m products) per unit, counted as dense
+ *          products even where symmetry halves the executed work;
+ *   bytes  elementwise kernels: bytes each element must move (momentum:
+ *          G + M read + M write + U write; AdamW: W r/w, G, m r/w, v r/w).
+ * muon_timing_collect waits for the recorded events, writes one entry per
+ * family into out (up to cap), sets *n to the number of families seen, and
+ * clears the records. */
+typedef struct {
+  char name[32];
+  int64_t launches;
+  double total_ms;
+  double flops;
+  double bytes;
+} muon_kernel_timing;
+
+muon_status muon_timing_enable(int32_t enable);
+muon_status muon_timing_collect(muon_kernel_timing* out, int32_t cap, int32_t* n);
+
 /* Static text for a status code. */
 const char* muon_status_string(int32_t status);
 

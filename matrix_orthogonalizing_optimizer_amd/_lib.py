@@ -24,7 +24,8 @@ MUON_KIND_MUON, MUON_KIND_ADAMW = 0, 1
 
 EXPORTED = ["muon_plan_create", "muon_plan_destroy", "muon_plan_workspace_bytes",
             "muon_plan_buckets", "muon_plan_units", "muon_step", "ns_orthogonalize",
-            "ns_orthogonalize_workspace_bytes", "muon_status_string", "muon_version"]
+            "ns_orthogonalize_workspace_bytes", "muon_timing_enable", "muon_timing_collect",
+            "muon_status_string", "muon_version"]
 
 
 class MuonError(RuntimeError):
@@ -55,6 +56,12 @@ class MuonHparams(ctypes.Structure):
 
 class MuonPlanOptions(ctypes.Structure):
     _fields_ = [("ns_method", ctypes.c_int32), ("ns_dtype", ctypes.c_int32)]
+
+
+class MuonKernelTiming(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int64),
+                ("total_ms", ctypes.c_double), ("flops", ctypes.c_double),
+                ("bytes", ctypes.c_double)]
 
 
 _lib = None
@@ -88,6 +95,10 @@ def lib():
     L.ns_orthogonalize.restype = i32
     L.ns_orthogonalize_workspace_bytes.argtypes = [i64, i64, i32, i32, ctypes.POINTER(sz)]
     L.ns_orthogonalize_workspace_bytes.restype = i32
+    L.muon_timing_enable.argtypes = [i32]
+    L.muon_timing_enable.restype = i32
+    L.muon_timing_collect.argtypes = [ctypes.POINTER(MuonKernelTiming), i32, ctypes.POINTER(i32)]
+    L.muon_timing_collect.restype = i32
     L.muon_status_string.argtypes = [i32]
     L.muon_status_string.restype = ctypes.c_char_p
     L.muon_version.argtypes = []
@@ -244,6 +255,21 @@ def ns_orthogonalize(X, steps: int = 5, coeffs=None, method: int = MUON_NS_STAND
     _check("ns_orthogonalize",
            lib().ns_orthogonalize(_ptr(X), rows, cols, ld, dtype, steps,
                                   ca, method, _ptr(workspace), wsz, _stream(stream)))
+
+
+def muon_timing_enable(enable: bool = True) -> None:
+    _check("muon_timing_enable", lib().muon_timing_enable(1 if enable else 0))
+
+
+def muon_timing_collect() -> dict:
+    """{family: {"launches", "total_ms", "flops", "bytes"}} since the last collect."""
+    cap = 32
+    arr = (MuonKernelTiming * cap)()
+    n = ctypes.c_int32()
+    _check("muon_timing_collect", lib().muon_timing_collect(arr, cap, ctypes.byref(n)))
+    return {arr[i].name.decode(): {"launches": arr[i].launches, "total_ms": arr[i].total_ms,
+                                   "flops": arr[i].flops, "bytes": arr[i].bytes}
+            for i in range(min(n.value, cap))}
 
 
 def muon_status_string(status: int) -> str:

@@ -14,7 +14,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build", "libmuon")
 LIB = os.path.join(PKG, "libmuon.so")
 
-HIP_SOURCES = ["api.cpp", "kernels_elem.hip", "gemm_bf16.hip", "gemm_f16.hip", "gemm_f32.hip"]
+HIP_SOURCES = ["api.cpp", "timing.cpp", "kernels_elem.hip", "gemm_bf16.hip", "gemm_f16.hip",
+               "gemm_f32.hip"]
 HOST_SOURCES = ["plan.cpp"]
 ARCH = "gfx950"
 

@@ -27,6 +27,7 @@
 #include "launch.hpp"
 #include "libmuon.h"
 #include "plan.hpp"
+#include "timing.hpp"
 
 using namespace muon;
 
@@ -42,6 +43,7 @@ struct ChainParams {
   float lr, wd;
   int32_t final_mode;
   int32_t vec_ok;
+  int32_t has_mom;
 };
 
 int dt_dev(int32_t muon_dtype) { return muon_dtype == MUON_F32 ? DT_F32 : DT_BF16; }
@@ -94,8 +96,16 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
   ma.mu = cp.mu;
   ma.nesterov = cp.nesterov;
   ma.vec_ok = cp.vec_ok;
-  HIP_TRY(launch_momentum(pdt, cdt, b.tall != 0, ma, (int64_t)cnt * b.km_tiles, st));
-  HIP_TRY(launch_norm_finalize(d_part, b.km_tiles, d_aux, cnt, st));
+  const double elems = (double)cnt * (double)m * (double)n;
+  const double units = (double)cnt;
+  const double mm_n = units * 2.0 * (double)m * (double)m * (double)n;  // 2 m^2 n per unit
+  const double mmm = units * 2.0 * (double)m * (double)m * (double)m;   // 2 m^3 per unit
+  const double pes = b.pdtype == MUON_F32 ? 4.0 : 2.0;
+  const double km_bytes = elems * (pes + (cp.has_mom ? 8.0 : 0.0) + (double)es);
+  HIP_TRY(timed(F_MOMENTUM, 0.0, km_bytes, st, [&] {
+    return launch_momentum(pdt, cdt, b.tall != 0, ma, (int64_t)cnt * b.km_tiles, st);
+  }));
+  HIP_TRY(timed(F_NORM, 0.0, 0.0, st, [&] { return launch_norm_finalize(d_part, b.km_tiles, d_aux, cnt, st); }));
 
   const int T = b.tile;
   auto final_args = [&](GemmArgs& g) {
@@ -122,7 +132,7 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
       g.C = A; g.ldc = b.mp; g.sC = ss;
       g.alphaSel = k == 0 ? SEL_INV_S2 : SEL_ONE;
       g.aux = d_aux;
-      HIP_TRY(launch_gemm(T, cdt, cdt, false, true, EPI_SCALE, g, st));
+      HIP_TRY(timed(F_SYRK, mm_n, 0.0, st, [&] { return launch_gemm(T, cdt, cdt, false, true, EPI_SCALE, g, st); }));
       // B = c A A + b A
       g = gemm_args(T, cnt, (int)m, (int)m, (int)m, true);
       g.L = A; g.ldl = b.mp; g.sL = ss;
@@ -130,7 +140,7 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
       g.E = A; g.lde = b.mp; g.sE = ss;
       g.C = B; g.ldc = b.mp; g.sC = ss;
       g.alpha = cc; g.beta = cb; g.gamma = 0.f;
-      HIP_TRY(launch_gemm(T, cdt, cdt, false, true, EPI_POLY, g, st));
+      HIP_TRY(timed(F_POLY, mmm, 0.0, st, [&] { return launch_gemm(T, cdt, cdt, false, true, EPI_POLY, g, st); }));
       // X' = a X + B X  (k = 0: (a U + B U) / s)
       g = gemm_args(T, cnt, (int)m, (int)n, (int)m, false);
       g.L = B; g.ldl = b.mp; g.sL = ss;
@@ -141,10 +151,11 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
       g.alphaSel = k == 0 ? SEL_INV_S : SEL_ONE;
       g.aux = d_aux;
       if (k + 1 < cp.steps) {
-        HIP_TRY(launch_gemm(T, cdt, cdt, true, false, EPI_AXPY, g, st));
+        HIP_TRY(timed(F_UPDATE, mm_n, 0.0, st, [&] { return launch_gemm(T, cdt, cdt, true, false, EPI_AXPY, g, st); }));
       } else {
         final_args(g);
-        HIP_TRY(launch_gemm(T, cdt, cdt, true, false, EPI_FINAL, g, st));
+        HIP_TRY(timed(F_FINAL, mm_n, elems * 2.0 * pes, st,
+                      [&] { return launch_gemm(T, cdt, cdt, true, false, EPI_FINAL, g, st); }));
       }
     }
     return MUON_OK;
@@ -163,13 +174,12 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
   char* R = data + b.off[1];
   char* Tm = data + b.off[2];
   char* QP[3] = {data + b.off[3], data + b.off[4], data + b.off[5]};
-  (void)es;
   GemmArgs g = gemm_args(T, cnt, (int)m, (int)m, (int)n, true);
   g.L = X0; g.ldl = b.ldx; g.sL = sx;
   g.R = X0; g.ldr = b.ldx; g.sR = sx;
   g.C = R; g.ldc = b.mp; g.sC = ss;
   g.alpha = rs; g.alphaSel = SEL_INV_S2; g.aux = d_aux;
-  HIP_TRY(launch_gemm(T, cdt, sdt, false, true, EPI_SCALE, g, st));
+  HIP_TRY(timed(F_GRAM_R0, mm_n, 0.0, st, [&] { return launch_gemm(T, cdt, sdt, false, true, EPI_SCALE, g, st); }));
   int q = -1;  // index of the buffer holding Q
   for (int k = 0; k < cp.steps; ++k) {
     const bool last = k + 1 == cp.steps;
@@ -183,7 +193,9 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
     g.E = R; g.lde = b.mp; g.sE = ss;
     g.C = QP[p]; g.ldc = b.mp; g.sC = ss;
     g.alpha = cc / (rs * rs); g.beta = cb / rs; g.gamma = ca;
-    HIP_TRY(launch_gemm(T, sdt, (last && k == 0) ? qdt_last : sdt, false, true, EPI_POLY, g, st));
+    HIP_TRY(timed(F_GRAM_P, mmm, 0.0, st, [&] {
+      return launch_gemm(T, sdt, (last && k == 0) ? qdt_last : sdt, false, true, EPI_POLY, g, st);
+    }));
     if (k == 0) {
       q = p;
     } else {
@@ -195,7 +207,8 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
       g.R = QP[q]; g.ldr = b.mp; g.sR = ss;
       g.C = QP[qn]; g.ldc = b.mp; g.sC = ss;
       g.beta = 0.f;
-      HIP_TRY(launch_gemm(T, sdt, last ? qdt_last : sdt, true, false, EPI_AXPY, g, st));
+      HIP_TRY(timed(F_GRAM_Q, mmm, 0.0, st,
+                    [&] { return launch_gemm(T, sdt, last ? qdt_last : sdt, true, false, EPI_AXPY, g, st); }));
       q = qn;
     }
     if (!last) {
@@ -205,13 +218,13 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
       g.R = R; g.ldr = b.mp; g.sR = ss;
       g.C = Tm; g.ldc = b.mp; g.sC = ss;
       g.beta = 0.f;
-      HIP_TRY(launch_gemm(T, sdt, sdt, false, false, EPI_AXPY, g, st));
+      HIP_TRY(timed(F_GRAM_T, mmm, 0.0, st, [&] { return launch_gemm(T, sdt, sdt, false, false, EPI_AXPY, g, st); }));
       // R = Tm P  (P symmetric; result symmetric: upper tiles + mirror)
       g = gemm_args(T, cnt, (int)m, (int)m, (int)m, true);
       g.L = Tm; g.ldl = b.mp; g.sL = ss;
       g.R = QP[p]; g.ldr = b.mp; g.sR = ss;
       g.C = R; g.ldc = b.mp; g.sC = ss;
-      HIP_TRY(launch_gemm(T, sdt, sdt, false, true, EPI_SCALE, g, st));
+      HIP_TRY(timed(F_GRAM_R, mmm, 0.0, st, [&] { return launch_gemm(T, sdt, sdt, false, true, EPI_SCALE, g, st); }));
     }
   }
   // O = Q X0 / s, fused with the update
@@ -223,7 +236,8 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
   g.alphaSel = SEL_INV_S;
   g.aux = d_aux;
   final_args(g);
-  HIP_TRY(launch_gemm(T, cdt, cdt, true, false, EPI_FINAL, g, st));
+  HIP_TRY(timed(F_FINAL, mm_n, elems * 2.0 * pes, st,
+                [&] { return launch_gemm(T, cdt, cdt, true, false, EPI_FINAL, g, st); }));
   return MUON_OK;
 }
 
@@ -378,6 +392,7 @@ muon_status muon_step(const muon_plan* plan, const muon_param_ptrs* ptrs, int32_
   }
   std::vector<AdamDesc> ad;
   int64_t adam_blocks = 0;
+  double adam_bytes = 0.0;
   for (int32_t p : P.adam) {
     const muon_param_shape& s = P.table[p];
     const int64_t numel = s.rows * s.cols;
@@ -395,6 +410,7 @@ muon_status muon_step(const muon_plan* plan, const muon_param_ptrs* ptrs, int32_
     d.vec_ok = aligned(q.param, 16) && aligned(q.grad, 16) && aligned(q.exp_avg, 16) &&
                aligned(q.exp_avg_sq, 16);
     adam_blocks += ceil_div(numel, ADAM_EPB);
+    adam_bytes += (double)numel * (s.dtype == MUON_F32 ? 28.0 : 22.0);
     ad.push_back(d);
   }
   UnitDesc* d_desc = reinterpret_cast<UnitDesc*>(ws + P.lay.off_desc);
@@ -412,6 +428,7 @@ muon_status muon_step(const muon_plan* plan, const muon_param_ptrs* ptrs, int32_
   cp.lr = hp->lr;
   cp.wd = hp->weight_decay;
   cp.final_mode = FINAL_UPDATE;
+  cp.has_mom = 1;
   float4* d_aux = reinterpret_cast<float4*>(ws + P.lay.off_aux);
   float* d_part = reinterpret_cast<float*>(ws + P.lay.off_part);
   char* data = ws + P.lay.off_data;
@@ -441,7 +458,7 @@ muon_status muon_step(const muon_plan* plan, const muon_param_ptrs* ptrs, int32_
     const double bc1 = 1.0 - std::pow((double)hp->adam_beta1, t);
     const double bc2 = 1.0 - std::pow((double)hp->adam_beta2, t);
     aa.step = (float)((double)hp->adam_lr * std::sqrt(bc2) / bc1);
-    HIP_TRY(launch_adamw(aa, adam_blocks, st_));
+    HIP_TRY(timed(F_ADAMW, 0.0, adam_bytes, st_, [&] { return launch_adamw(aa, adam_blocks, st_); }));
   }
   return MUON_OK;
 }
@@ -523,6 +540,7 @@ muon_status ns_orthogonalize(void* X, int64_t rows, int64_t cols, int64_t ld, in
   cp.lr = 0.f;
   cp.wd = 0.f;
   cp.final_mode = FINAL_STORE;
+  cp.has_mom = 0;
   cp.vec_ok = aligned(X, 16) && (ld % 8 == 0);
   return run_chunk(b, reinterpret_cast<UnitDesc*>(ws), reinterpret_cast<float4*>(ws + off_aux),
                    reinterpret_cast<float*>(ws + off_part), ws + off_data, 1, cp, st_);

@@ -50,10 +50,14 @@ template <> struct Mfma<f16> {
 template <> struct Mfma<float> {
   static constexpr int EPC = 4;
   __device__ __forceinline__ static void run(f32x16& acc, const u32x4& a, const u32x4& b) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a[e]),
-                                                 __builtin_bit_cast(float, b[e]), acc, 0, 0, 0);
+    // bit-cast the whole vector: a bit-cast of one vector-element lvalue
+    // was lowered to element 0 for every e
+    const f32x4 af = __builtin_bit_cast(f32x4, a);
+    const f32x4 bf = __builtin_bit_cast(f32x4, b);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[0], bf[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[1], bf[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[2], bf[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[3], bf[3], acc, 0, 0, 0);
   }
 };
 
@@ -326,6 +330,19 @@ void gemm_kernel(const GemmArgs a) {
               }
             }
           }
+        } else if (SYM && bi == bj) {
+          // diagonal tile of a symmetric product: the upper triangle is
+          // stored and mirrored, so the result is exactly symmetric even
+          // when L . R^T is symmetric only up to rounding
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int gi = gi0 + r;
+            if (gi <= gj && gi < a.M && gj < a.ldc) {
+              const TO val = from_f32<TO>(v[r]);
+              Cp[(int64_t)gi * a.ldc + gj] = val;
+              if (gi < gj && gj < a.M) Cp[(int64_t)gj * a.ldc + gi] = val;
+            }
+          }
         } else {
           // direct tile
           if (gj < a.ldc) {
@@ -335,7 +352,7 @@ void gemm_kernel(const GemmArgs a) {
           }
           // mirror tile of a symmetric product: 4 consecutive columns of row gj
           if constexpr (SYM) {
-            if (bi != bj && gj < a.M && gi0 < a.ldc) {
+            if (gj < a.M && gi0 < a.ldc) {
               TO* dst = Cp + (int64_t)gj * a.ldc + gi0;
               if constexpr (sizeof(TO) == 2) {
                 u32x2 p;

@@ -25,6 +25,12 @@ def rel(a, b) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
 
 
+def stored(x: np.ndarray, dtype) -> np.ndarray:
+    """An fp64 oracle result rounded (RNE) to the storage dtype of the
+    tensor it is compared with, back in fp64."""
+    return torch.from_numpy(np.asarray(x, dtype=np.float64)).to(dtype).to(torch.float64).numpy()
+
+
 def to_dev(x, dtype, device):
     return torch.as_tensor(np.asarray(x)).to(device=device, dtype=dtype).contiguous()
 

@@ -20,6 +20,14 @@ F32, BF16 = 0, 1
 Row = Tuple[int, int, int, int, int, int]
 
 
+def _hp(**kw):
+    base = dict(lr=0.02, momentum=0.95, weight_decay=0.1, nesterov=True, ns_steps=5,
+                adam_lr=3e-4, adam_beta1=0.9, adam_beta2=0.95, adam_eps=1e-8,
+                adam_weight_decay=0.1)
+    base.update(kw)
+    return base
+
+
 @dataclass
 class Workload:
     name: str
@@ -28,15 +36,7 @@ class Workload:
     rank: int                 # rank of the synthetic low-rank gradient
     steps: int = 1            # optimizer steps the workload runs
     method: str = "standard"  # ns method
-    hp: dict = field(default_factory=dict)
-
-
-def _hp(**kw):
-    base = dict(lr=0.02, momentum=0.95, weight_decay=0.1, nesterov=True, ns_steps=5,
-                adam_lr=3e-4, adam_beta1=0.9, adam_beta2=0.95, adam_eps=1e-8,
-                adam_weight_decay=0.1)
-    base.update(kw)
-    return base
+    hp: dict = field(default_factory=_hp)
 
 
 def single_256x512() -> Workload:
