@@ -44,6 +44,7 @@ struct ChainParams {
   int32_t final_mode;
   int32_t vec_ok;
   int32_t has_mom;
+  int32_t wvec;  // parameter / update_out rows 16-byte aligned (fused update epilogue)
 };
 
 int dt_dev(int32_t muon_dtype) { return muon_dtype == MUON_F32 ? DT_F32 : DT_BF16; }
@@ -115,6 +116,7 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
     g.finalMode = cp.final_mode;
     g.tall = b.tall;
     g.wdtype = pdt;
+    g.wvec = cp.wvec;
   };
 
   if (b.method == MUON_NS_STANDARD) {
@@ -435,12 +437,14 @@ muon_status muon_step(const muon_plan* plan, const muon_param_ptrs* ptrs, int32_
   for (const PlanBucket& b : P.buckets) {
     for (int32_t s0 = 0; s0 < b.count; s0 += b.chunk) {
       const int32_t cnt = std::min(b.chunk, b.count - s0);
-      bool vec = true;
-      for (int32_t i = 0; i < cnt && vec; ++i) {
+      bool vec = true, wv = true;
+      for (int32_t i = 0; i < cnt; ++i) {
         const UnitDesc& d = hd[(size_t)b.first + s0 + i];
-        vec = aligned(d.g, 16) && aligned(d.mom, 16) && (d.ld % 8 == 0);
+        vec = vec && aligned(d.g, 16) && aligned(d.mom, 16) && (d.ld % 8 == 0);
+        wv = wv && aligned(d.w, 16) && (!d.o || aligned(d.o, 16)) && (d.ld % 8 == 0);
       }
       cp.vec_ok = vec ? 1 : 0;
+      cp.wvec = wv ? 1 : 0;
       st = run_chunk(b, d_desc + b.first + s0, d_aux, d_part, data, cnt, cp, st_);
       if (st != MUON_OK) return st;
     }
@@ -486,6 +490,7 @@ static muon_status ns_bucket(int64_t rows, int64_t cols, int32_t dtype, int32_t 
   b.first = 0;
   b.count = 1;
   bucket_derive(b, ~size_t(0));
+  if (!bucket_addressable(b)) return MUON_E_SHAPE;
   return MUON_OK;
 }
 
@@ -542,6 +547,7 @@ muon_status ns_orthogonalize(void* X, int64_t rows, int64_t cols, int64_t ld, in
   cp.final_mode = FINAL_STORE;
   cp.has_mom = 0;
   cp.vec_ok = aligned(X, 16) && (ld % 8 == 0);
+  cp.wvec = cp.vec_ok;
   return run_chunk(b, reinterpret_cast<UnitDesc*>(ws), reinterpret_cast<float4*>(ws + off_aux),
                    reinterpret_cast<float*>(ws + off_part), ws + off_data, 1, cp, st_);
 }

@@ -26,6 +26,7 @@ struct GemmArgs {
   int32_t finalMode;       // FINAL_UPDATE or FINAL_STORE
   int32_t tall;            // EPI_FINAL: the unit is the transpose of the parameter block
   int32_t wdtype;          // EPI_FINAL: DT_F32 or DT_BF16
+  int32_t wvec;            // EPI_FINAL: parameter / update_out rows are 16-byte aligned, ld % 8 == 0
 };
 
 // Momentum kernel (see elementwise.hpp).

@@ -29,6 +29,11 @@ size_t per_unit_data_bytes(const PlanBucket& b) {
   return 2 * xb + 2 * sb;
 }
 
+bool bucket_addressable(const PlanBucket& b) {
+  // every GEMM operand of one unit is addressed with 32-bit byte offsets
+  return (uint64_t)b.m * (uint64_t)b.ldx * (uint64_t)elem_size(b.cdtype) < (uint64_t(1) << 31);
+}
+
 void bucket_derive(PlanBucket& b, size_t chunk_cap_bytes) {
   b.ldx = round_up(b.n, 8);
   b.mp = round_up(b.m, 8);
@@ -127,6 +132,7 @@ muon_status build_plan(const muon_param_shape* table, int32_t n, const muon_plan
     b.count = (int32_t)members[bi].size();
     for (int32_t i : members[bi]) P.units.push_back(order[i]);
     bucket_derive(b, CHUNK_CAP_BYTES);
+    if (!bucket_addressable(b)) return MUON_E_SHAPE;
     P.max_chunk = std::max(P.max_chunk, b.chunk);
     P.max_partials = std::max<int64_t>(P.max_partials, (int64_t)b.chunk * b.km_tiles);
     P.max_data = std::max(P.max_data, b.data_bytes);
