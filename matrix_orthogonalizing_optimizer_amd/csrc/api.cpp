@@ -73,21 +73,29 @@ GemmArgs gemm_args(int tile, int32_t cnt, int M, int N, int K, bool sym) {
   } while (0)
 
 // Momentum + norm for one chunk, then the Newton-Schulz chain and the fused
-// update (or plain store of O for ns_orthogonalize).
+// update (or a plain store of O for ns_orthogonalize).  Every unit is kept in
+// both orientations: X (m x n, wide) and Y = X^T (n x m).
 muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux, float* d_part,
                       char* data, int32_t cnt, const ChainParams& cp, hipStream_t st) {
   const int cdt = dt_dev(b.cdtype);
   const int pdt = dt_dev(b.pdtype);
   const int es = elem_size(b.cdtype);
   const int64_t m = b.m, n = b.n;
-  const int64_t sx = m * b.ldx, ss = m * b.mp;
+  const int64_t sx = m * b.ldx, sy = n * b.mp, ss = m * b.mp;
+  char* X = data + b.off[0];
+  char* Y0 = data + b.off[1];
 
+  // K-M: the parameter block is X (wide unit) or Y (tall unit); the kernel
+  // writes it as is and transposed
   MomArgs ma;
   std::memset(&ma, 0, sizeof(ma));
   ma.desc = d_desc;
-  ma.X0 = data + b.off[0];
-  ma.ldx = b.ldx;
-  ma.sX = sx;
+  ma.D = b.tall ? Y0 : X;
+  ma.ldd = b.tall ? b.mp : b.ldx;
+  ma.sD = b.tall ? sy : sx;
+  ma.T = b.tall ? X : Y0;
+  ma.ldt = b.tall ? b.ldx : b.mp;
+  ma.sT = b.tall ? sx : sy;
   ma.partials = d_part;
   ma.rows = (int32_t)(b.tall ? n : m);
   ma.cols = (int32_t)(b.tall ? m : n);
@@ -102,7 +110,7 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
   const double mm_n = units * 2.0 * (double)m * (double)m * (double)n;  // 2 m^2 n per unit
   const double mmm = units * 2.0 * (double)m * (double)m * (double)m;   // 2 m^3 per unit
   const double pes = b.pdtype == MUON_F32 ? 4.0 : 2.0;
-  const double km_bytes = elems * (pes + (cp.has_mom ? 8.0 : 0.0) + (double)es);
+  const double km_bytes = elems * (pes + (cp.has_mom ? 8.0 : 0.0) + 2.0 * (double)es);
   HIP_TRY(timed(F_MOMENTUM, 0.0, km_bytes, st, [&] {
     return launch_momentum(pdt, cdt, b.tall != 0, ma, (int64_t)cnt * b.km_tiles, st);
   }));
@@ -118,128 +126,125 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
     g.wdtype = pdt;
     g.wvec = cp.wvec;
   };
+  // symmetric product L . R^T of m x m output into C (both triangles)
+  auto sym_args = [&](const void* L, int64_t ldl, int64_t sL, const void* R, int64_t ldr, int64_t sR,
+                      int K, void* C) {
+    GemmArgs g = gemm_args(T, cnt, (int)m, (int)m, K, true);
+    g.L = L; g.ldl = ldl; g.sL = sL;
+    g.R = R; g.ldr = ldr; g.sR = sR;
+    g.C = C; g.ldc = b.mp; g.sC = ss;
+    g.C2 = C; g.ldc2 = b.mp; g.sC2 = ss;
+    return g;
+  };
 
   if (b.method == MUON_NS_STANDARD) {
-    char* X[2] = {data + b.off[0], data + b.off[1]};
-    char* A = data + b.off[2];
-    char* B = data + b.off[3];
+    char* Y[2] = {Y0, data + b.off[2]};
+    char* A = data + b.off[3];
+    char* B = data + b.off[4];
     for (int k = 0; k < cp.steps; ++k) {
       const float ca = cp.coeffs[3 * k], cb = cp.coeffs[3 * k + 1], cc = cp.coeffs[3 * k + 2];
-      char* Xi = X[k & 1];
-      char* Xo = X[(k + 1) & 1];
       // A = X X^T  (k = 0: U U^T / s^2)
-      GemmArgs g = gemm_args(T, cnt, (int)m, (int)m, (int)n, true);
-      g.L = Xi; g.ldl = b.ldx; g.sL = sx;
-      g.R = Xi; g.ldr = b.ldx; g.sR = sx;
-      g.C = A; g.ldc = b.mp; g.sC = ss;
+      GemmArgs g = sym_args(X, b.ldx, sx, X, b.ldx, sx, (int)n, A);
       g.alphaSel = k == 0 ? SEL_INV_S2 : SEL_ONE;
       g.aux = d_aux;
-      HIP_TRY(timed(F_SYRK, mm_n, 0.0, st, [&] { return launch_gemm(T, cdt, cdt, false, true, EPI_SCALE, g, st); }));
-      // B = c A A + b A
-      g = gemm_args(T, cnt, (int)m, (int)m, (int)m, true);
-      g.L = A; g.ldl = b.mp; g.sL = ss;
-      g.R = A; g.ldr = b.mp; g.sR = ss;
+      HIP_TRY(timed(F_SYRK, mm_n, 0.0, st, [&] { return launch_gemm(T, cdt, cdt, true, EPI_SCALE, g, st); }));
+      // B = c A A^T + b A
+      g = sym_args(A, b.mp, ss, A, b.mp, ss, (int)m, B);
       g.E = A; g.lde = b.mp; g.sE = ss;
-      g.C = B; g.ldc = b.mp; g.sC = ss;
       g.alpha = cc; g.beta = cb; g.gamma = 0.f;
-      HIP_TRY(timed(F_POLY, mmm, 0.0, st, [&] { return launch_gemm(T, cdt, cdt, false, true, EPI_POLY, g, st); }));
-      // X' = a X + B X  (k = 0: (a U + B U) / s)
-      g = gemm_args(T, cnt, (int)m, (int)n, (int)m, false);
-      g.L = B; g.ldl = b.mp; g.sL = ss;
-      g.R = Xi; g.ldr = b.ldx; g.sR = sx;
-      g.E = Xi; g.lde = b.ldx; g.sE = sx;
-      g.C = Xo; g.ldc = b.ldx; g.sC = sx;
+      HIP_TRY(timed(F_POLY, mmm, 0.0, st, [&] { return launch_gemm(T, cdt, cdt, true, EPI_POLY, g, st); }));
+      // Y' = a Y + Y B^T  (k = 0: (a U + B U)^T / s); stores Y' and X' = Y'^T
+      g = gemm_args(T, cnt, (int)n, (int)m, (int)m, false);
+      g.L = Y[k & 1]; g.ldl = b.mp; g.sL = sy;
+      g.R = B; g.ldr = b.mp; g.sR = ss;
+      g.E = Y[k & 1]; g.lde = b.mp; g.sE = sy;
       g.alpha = 1.f; g.beta = ca;
       g.alphaSel = k == 0 ? SEL_INV_S : SEL_ONE;
       g.aux = d_aux;
       if (k + 1 < cp.steps) {
-        HIP_TRY(timed(F_UPDATE, mm_n, 0.0, st, [&] { return launch_gemm(T, cdt, cdt, true, false, EPI_AXPY, g, st); }));
+        g.C = Y[(k + 1) & 1]; g.ldc = b.mp; g.sC = sy;
+        g.C2 = X; g.ldc2 = b.ldx; g.sC2 = sx;
+        HIP_TRY(timed(F_UPDATE, mm_n, 0.0, st, [&] { return launch_gemm(T, cdt, cdt, false, EPI_AXPY, g, st); }));
       } else {
         final_args(g);
         HIP_TRY(timed(F_FINAL, mm_n, elems * 2.0 * pes, st,
-                      [&] { return launch_gemm(T, cdt, cdt, true, false, EPI_FINAL, g, st); }));
+                      [&] { return launch_gemm(T, cdt, cdt, false, EPI_FINAL, g, st); }));
       }
     }
     return MUON_OK;
   }
 
   // Gram chain: m x m work in fp16 (bf16 bucket) or fp32, R scaled by 2^e.
+  // Z = Q^T is kept: Z' = Z P (P symmetric); the last product stores Q = Z'^T.
   const int sdt = cdt == DT_F32 ? DT_F32 : DT_F16;
-  const int qdt_last = cdt == DT_F32 ? DT_F32 : DT_BF16;  // Q feeds the final GEMM with X0
+  const int qdt_last = cdt == DT_F32 ? DT_F32 : DT_BF16;  // Q feeds the final GEMM with Y0
   float rs = 1.f;
   if (sdt == DT_F16) {
     int e = 0;
     while ((int64_t(1) << e) < m && e < 15) ++e;
     rs = std::ldexp(1.f, e);
   }
-  char* X0 = data + b.off[0];
-  char* R = data + b.off[1];
-  char* Tm = data + b.off[2];
-  char* QP[3] = {data + b.off[3], data + b.off[4], data + b.off[5]};
-  GemmArgs g = gemm_args(T, cnt, (int)m, (int)m, (int)n, true);
-  g.L = X0; g.ldl = b.ldx; g.sL = sx;
-  g.R = X0; g.ldr = b.ldx; g.sR = sx;
-  g.C = R; g.ldc = b.mp; g.sC = ss;
+  char* R = data + b.off[2];
+  char* Tm = data + b.off[3];
+  char* PZ[3] = {data + b.off[4], data + b.off[5], data + b.off[6]};
+  GemmArgs g = sym_args(X, b.ldx, sx, X, b.ldx, sx, (int)n, R);
   g.alpha = rs; g.alphaSel = SEL_INV_S2; g.aux = d_aux;
-  HIP_TRY(timed(F_GRAM_R0, mm_n, 0.0, st, [&] { return launch_gemm(T, cdt, sdt, false, true, EPI_SCALE, g, st); }));
-  int q = -1;  // index of the buffer holding Q
+  HIP_TRY(timed(F_GRAM_R0, mm_n, 0.0, st, [&] { return launch_gemm(T, cdt, sdt, true, EPI_SCALE, g, st); }));
+  int z = -1;  // buffer holding Z (after the last step: Q)
   for (int k = 0; k < cp.steps; ++k) {
     const bool last = k + 1 == cp.steps;
     const float ca = cp.coeffs[3 * k], cb = cp.coeffs[3 * k + 1], cc = cp.coeffs[3 * k + 2];
     int p = 0;
-    while (p == q) ++p;
-    // P = a I + (b / rs) R + (c / rs^2) R R
-    g = gemm_args(T, cnt, (int)m, (int)m, (int)m, true);
-    g.L = R; g.ldl = b.mp; g.sL = ss;
-    g.R = R; g.ldr = b.mp; g.sR = ss;
+    while (p == z) ++p;
+    // P = a I + (b / rs) R + (c / rs^2) R R^T
+    g = sym_args(R, b.mp, ss, R, b.mp, ss, (int)m, PZ[p]);
     g.E = R; g.lde = b.mp; g.sE = ss;
-    g.C = QP[p]; g.ldc = b.mp; g.sC = ss;
     g.alpha = cc / (rs * rs); g.beta = cb / rs; g.gamma = ca;
     HIP_TRY(timed(F_GRAM_P, mmm, 0.0, st, [&] {
-      return launch_gemm(T, sdt, (last && k == 0) ? qdt_last : sdt, false, true, EPI_POLY, g, st);
+      return launch_gemm(T, sdt, (last && k == 0) ? qdt_last : sdt, true, EPI_POLY, g, st);
     }));
     if (k == 0) {
-      q = p;
+      z = p;  // Z_0 = P_0^T = P_0
     } else {
-      int qn = 0;
-      while (qn == q || qn == p) ++qn;
-      // Q' = P Q
+      int zn = 0;
+      while (zn == z || zn == p) ++zn;
+      // Z' = Z P; the last one is stored transposed, as Q
       g = gemm_args(T, cnt, (int)m, (int)m, (int)m, false);
-      g.L = QP[p]; g.ldl = b.mp; g.sL = ss;
-      g.R = QP[q]; g.ldr = b.mp; g.sR = ss;
-      g.C = QP[qn]; g.ldc = b.mp; g.sC = ss;
+      g.L = PZ[z]; g.ldl = b.mp; g.sL = ss;
+      g.R = PZ[p]; g.ldr = b.mp; g.sR = ss;
       g.beta = 0.f;
+      if (last) {
+        g.C2 = PZ[zn]; g.ldc2 = b.mp; g.sC2 = ss;
+      } else {
+        g.C = PZ[zn]; g.ldc = b.mp; g.sC = ss;
+      }
       HIP_TRY(timed(F_GRAM_Q, mmm, 0.0, st,
-                    [&] { return launch_gemm(T, sdt, last ? qdt_last : sdt, true, false, EPI_AXPY, g, st); }));
-      q = qn;
+                    [&] { return launch_gemm(T, sdt, last ? qdt_last : sdt, false, EPI_AXPY, g, st); }));
+      z = zn;
     }
     if (!last) {
-      // Tm = P R  (R symmetric: read as R^T rows)
+      // Tm = P R  (R symmetric: its rows serve as R^T)
       g = gemm_args(T, cnt, (int)m, (int)m, (int)m, false);
-      g.L = QP[p]; g.ldl = b.mp; g.sL = ss;
+      g.L = PZ[p]; g.ldl = b.mp; g.sL = ss;
       g.R = R; g.ldr = b.mp; g.sR = ss;
       g.C = Tm; g.ldc = b.mp; g.sC = ss;
       g.beta = 0.f;
-      HIP_TRY(timed(F_GRAM_T, mmm, 0.0, st, [&] { return launch_gemm(T, sdt, sdt, false, false, EPI_AXPY, g, st); }));
-      // R = Tm P  (P symmetric; result symmetric: upper tiles + mirror)
-      g = gemm_args(T, cnt, (int)m, (int)m, (int)m, true);
-      g.L = Tm; g.ldl = b.mp; g.sL = ss;
-      g.R = QP[p]; g.ldr = b.mp; g.sR = ss;
-      g.C = R; g.ldc = b.mp; g.sC = ss;
-      HIP_TRY(timed(F_GRAM_R, mmm, 0.0, st, [&] { return launch_gemm(T, sdt, sdt, false, true, EPI_SCALE, g, st); }));
+      HIP_TRY(timed(F_GRAM_T, mmm, 0.0, st, [&] { return launch_gemm(T, sdt, sdt, false, EPI_AXPY, g, st); }));
+      // R = Tm P  (P symmetric; the result is symmetric: upper tiles + mirror)
+      g = sym_args(Tm, b.mp, ss, PZ[p], b.mp, ss, (int)m, R);
+      HIP_TRY(timed(F_GRAM_R, mmm, 0.0, st, [&] { return launch_gemm(T, sdt, sdt, true, EPI_SCALE, g, st); }));
     }
   }
-  // O = Q X0 / s, fused with the update
-  g = gemm_args(T, cnt, (int)m, (int)n, (int)m, false);
-  g.L = QP[q]; g.ldl = b.mp; g.sL = ss;
-  g.R = X0; g.ldr = b.ldx; g.sR = sx;
-  g.E = X0; g.lde = b.ldx; g.sE = sx;
+  // O^T = Y0 Q^T / s  (= (Q X0)^T / s), fused with the update
+  g = gemm_args(T, cnt, (int)n, (int)m, (int)m, false);
+  g.L = Y0; g.ldl = b.mp; g.sL = sy;
+  g.R = PZ[z]; g.ldr = b.mp; g.sR = ss;
   g.beta = 0.f;
   g.alphaSel = SEL_INV_S;
   g.aux = d_aux;
   final_args(g);
   HIP_TRY(timed(F_FINAL, mm_n, elems * 2.0 * pes, st,
-                [&] { return launch_gemm(T, cdt, cdt, true, false, EPI_FINAL, g, st); }));
+                [&] { return launch_gemm(T, cdt, cdt, false, EPI_FINAL, g, st); }));
   return MUON_OK;
 }
 

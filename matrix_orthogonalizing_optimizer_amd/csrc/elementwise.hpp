@@ -19,7 +19,7 @@ namespace muon {
 // Each workgroup writes one partial sum of U^2 (fp32, fixed order).
 // ---------------------------------------------------------------------------
 
-template <typename TG, typename TX, bool TALL>
+template <typename TG, typename TX>
 __global__ __launch_bounds__(256) void momentum_kernel(const MomArgs a) {
   __shared__ float tile[KM_TR][KM_TC + 1];
   __shared__ float red[4];
@@ -30,7 +30,8 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MomArgs a) {
   const UnitDesc d = a.desc[unit];
   const TG* __restrict__ G = reinterpret_cast<const TG*>(d.g);
   float* __restrict__ M = d.mom;
-  TX* __restrict__ X = reinterpret_cast<TX*>(a.X0) + (int64_t)unit * a.sX;
+  TX* __restrict__ X = reinterpret_cast<TX*>(a.D) + (int64_t)unit * a.sD;
+  TX* __restrict__ XT = reinterpret_cast<TX*>(a.T) + (int64_t)unit * a.sT;
 
   const int tid = threadIdx.x;
   const int cg = tid & 15;   // 8-column group
@@ -96,37 +97,34 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MomArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss = fmaf(u[e], u[e], ss);
     }
-    if constexpr (!TALL) {
-      // X0 row r, columns c..c+8 (columns past cols are zero padding)
-      if (r < a.rows && c < a.cols) {
-        TX* dst = X + (int64_t)r * a.ldx + c;
-        if constexpr (sizeof(TX) == 2) {
-          u32x4 p;
+    // own layout: row r, columns c..c+8 (columns past cols are zero padding)
+    if (r < a.rows && c < a.cols) {
+      TX* dst = X + (int64_t)r * a.ldd + c;
+      if constexpr (sizeof(TX) == 2) {
+        u32x4 p;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            p[j] = (uint32_t)bits16(from_f32<TX>(u[2 * j])) |
-                   ((uint32_t)bits16(from_f32<TX>(u[2 * j + 1])) << 16);
-          *reinterpret_cast<u32x4*>(dst) = p;
-        } else {
-          *reinterpret_cast<f32x4*>(dst) = f32x4{u[0], u[1], u[2], u[3]};
-          *reinterpret_cast<f32x4*>(dst + 4) = f32x4{u[4], u[5], u[6], u[7]};
-        }
+        for (int j = 0; j < 4; ++j)
+          p[j] = (uint32_t)bits16(from_f32<TX>(u[2 * j])) |
+                 ((uint32_t)bits16(from_f32<TX>(u[2 * j + 1])) << 16);
+        *reinterpret_cast<u32x4*>(dst) = p;
+      } else {
+        *reinterpret_cast<f32x4*>(dst) = f32x4{u[0], u[1], u[2], u[3]};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{u[4], u[5], u[6], u[7]};
       }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) tile[lr][cg * 8 + e] = u[e];
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[lr][cg * 8 + e] = u[e];
   }
-  if constexpr (TALL) {
+  {
     __syncthreads();
-    // X0 row (c0 + c), columns r0 .. r0+32: 128 rows x 4 chunks of 8
+    // transposed layout: row (c0 + c), columns r0 .. r0+32: 128 rows x 4 chunks of 8
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int q = tid + 256 * j;
       const int c = q >> 2, rq = q & 3;
       const int gc = c0 + c, gr = r0 + rq * 8;
       if (gc < a.cols && gr < a.rows) {
-        TX* dst = X + (int64_t)gc * a.ldx + gr;
+        TX* dst = XT + (int64_t)gc * a.ldt + gr;
         float u[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) u[e] = tile[rq * 8 + e][c];

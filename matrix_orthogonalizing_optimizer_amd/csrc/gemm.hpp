@@ -1,36 +1,47 @@
 // Grouped MFMA GEMM for the Newton-Schulz contractions on gfx950.
 //
 // One launch computes, for every unit u of a bucket chunk,
-//     C_u = epilogue( L_u . op(R_u) )
-// where L_u is M x K row-major (K contiguous) and op(R_u) is either R_u^T
-// with R_u stored N x K (K contiguous, "RT") or R_u stored K x N (N
-// contiguous, "RN").  The Newton-Schulz step of "Muon Optimizer and the
-// Distributed Implementation" (section "Newton-Schulz Iteration"),
+//     C_u = epilogue( L_u . R_u^T )
+// with L_u (M x K) and R_u (N x K) both row-major with K contiguous.  The
+// Newton-Schulz step of "Muon Optimizer and the Distributed Implementation"
+// (section "Newton-Schulz Iteration"),
 //     A = X X^T,   B = b A + c A A,   X' = a X + B X,
-// maps onto it as: A and B are symmetric products (RT with R = L, only the
-// upper-triangle tiles computed and mirror-written), X' is an RN product.
+// is run with every unit kept in both orientations, X (m x n) and Y = X^T
+// (n x m): A = X X^T and B = c A A^T + b A are symmetric products (only
+// upper-triangle tiles are computed, then mirrored), and the update is
+// computed transposed, Y' = a Y + Y B^T (B is symmetric), its epilogue
+// storing Y' directly and X' = Y'^T through the mirror pass.  So both
+// operands of every product are K-contiguous.
 //
-// Tiling (CDNA4, wave64): a 256-thread workgroup owns a BM x BN output tile,
-// 2 x 2 waves each own (BM/2) x (BN/2) built from 32x32 MFMA tiles
-// (v_mfma_f32_32x32x16_{bf16,f16}; fp32 uses four v_mfma_f32_32x32x2_f32 per
-// 16-byte fragment).  K advances by 128 bytes per stage; operands are staged
-// global -> registers -> LDS with double-buffered LDS and an XOR swizzle over
-// 16-byte chunks so that fragment reads and stores are bank-conflict free.
-// RN operands are transposed in registers (8x8 16-bit or 4x4 32-bit blocks)
-// on their way to LDS, so every fragment read is a 16-byte ds_read along K.
+// Tiling (CDNA4, wave64): a 256-thread workgroup owns a BM x BN output tile
+// (256 x 256, or 128 x 128 for small m); 2 x 2 waves each own (BM/2) x (BN/2)
+// built from 32x32 MFMA tiles (v_mfma_f32_32x32x16_{bf16,f16}; fp32 issues
+// four v_mfma_f32_32x32x2_f32 per 16-byte fragment), accumulators in AGPRs.
 //
-// Bounds: operands are read with buffer loads over exactly the unit's
-// matrix; a chunk whose row is out of range, or whose first k is past K,
-// gets an out-of-range offset and reads as zero.  Along the contiguous
-// dimension a 16-byte chunk is read when its first element is in range,
-// which relies on leading dimensions that are multiples of 8 with zero
-// padding (the workspace layout guarantees it).  Every operand matrix must
-// be smaller than 2^31 bytes (checked by the planner).
+// Operand staging: K advances 64 bytes per stage.  Global -> LDS copies use
+// buffer_load_dwordx4 ... lds (each lane's 16 bytes land at M0 + 16 * lane),
+// four stages in flight in an LDS ring, so no registers hold staged data and
+// the wave never stalls on a copy it is about to store.  The lane -> chunk
+// assignment realises an XOR swizzle of the 16-byte chunks of each 64-byte
+// row that keeps the 32-row fragment reads conflict free.  Out-of-range rows
+// and K chunks get an out-of-range buffer offset and read as zero; along K a
+// 16-byte chunk is read when its first element is in range, which relies on
+// leading dimensions that are multiples of 8 with zero padding (the workspace
+// layout guarantees it).  Every operand matrix is smaller than 2^31 bytes
+// (checked by the planner).
+//
+// Schedule per stage (two k16 steps): step 0's MFMAs carry the fragment reads
+// of step 1; a barrier (after this wave's copies of the next stage landed)
+// separates the steps; step 1's MFMAs carry the next-next-next stage's copies
+// into the slot just freed and the fragment reads of the next stage's step 0.
+// A wave issues in order and an MFMA keeps the matrix pipe busy for 32
+// cycles, so each memory instruction is placed between two MFMAs.
 //
 // Epilogue: each wave stages its accumulators in LDS one 32-row strip at a
-// time and writes them back with 16-byte row-contiguous accesses (direct
-// pass) and, for symmetric products and tall-parameter updates, with the
-// strip transposed (mirror pass).
+// time, turns them into output values in place (scale, polynomial, axpy with
+// the addend E read as 16-byte rows), then stores the strip with 16-byte row
+// chunks (direct pass, to C) and/or transposed (mirror pass, to C2: the
+// symmetric mirror, X' of the update, or the transposed parameter block).
 #pragma once
 
 #include "kernel_args.hpp"
@@ -40,7 +51,7 @@ namespace muon {
 template <typename T> struct Mfma;
 
 template <> struct Mfma<bf16> {
-  static constexpr int EPC = 8;  // elements per 16-byte chunk
+  static constexpr int NI = 1;  // MFMA instructions per 16-byte fragment pair
   __device__ __forceinline__ static void run(f32x16& acc, const u32x4& a, const u32x4& b) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
@@ -48,7 +59,7 @@ template <> struct Mfma<bf16> {
 };
 
 template <> struct Mfma<f16> {
-  static constexpr int EPC = 8;
+  static constexpr int NI = 1;
   __device__ __forceinline__ static void run(f32x16& acc, const u32x4& a, const u32x4& b) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                  __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
@@ -56,7 +67,7 @@ template <> struct Mfma<f16> {
 };
 
 template <> struct Mfma<float> {
-  static constexpr int EPC = 4;
+  static constexpr int NI = 4;
   __device__ __forceinline__ static void run(f32x16& acc, const u32x4& a, const u32x4& b) {
     // bit-cast the whole vector: a bit-cast of one vector-element lvalue
     // was lowered to element 0 for every e
@@ -75,28 +86,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 }
 constexpr uint32_t OOB = 0x80000000u;
 
-__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt in bits 3:0
+// and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
-// Swizzled 16-byte slot of (row, chunk) in an LDS tile with 8 chunks per row.
-__device__ __forceinline__ int lds_slot(int row, int chunk) {
-  return row * 8 + (chunk ^ (row & 7) ^ ((row >> 3) & 7));
+// The same with lgkmcnt(0): this wave's LDS reads have completed as well.
+template <int N> __device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xf) | ((N >> 4) << 14) | (0x7 << 4));
 }
 
-// 8x8 transpose of 16-bit elements: in[r] holds row r (8 elements in 4
-// words); out[c] receives column c.
-__device__ __forceinline__ void transpose8x8_b16(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int w = c >> 1, sh = (c & 1) * 16;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t lo = (in[2 * j][w] >> sh) & 0xffffu;
-      uint32_t hi = (in[2 * j + 1][w] >> sh) & 0xffffu;
-      out[c][j] = lo | (hi << 16);
-    }
-  }
+// 16 bytes per lane from global memory straight into LDS at dst + 16 * lane.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, off, 0, 0, 0);
+}
+
+// 16-byte slot of (row, chunk) in a stage tile with 4 chunks per 64-byte row.
+__device__ __forceinline__ int lds_slot4(int row, int chunk) {
+  return row * 4 + (chunk ^ ((row >> 2) & 3));
 }
 
 // Upper-triangle tile t (row-major over bi <= bj) of a T x T tile grid.
@@ -139,8 +151,8 @@ template <typename T> __device__ __forceinline__ void store8(T* p, const float (
 }
 
 // Fused parameter update of 8 consecutive parameter elements (one row of the
-// parameter block, columns c..c+7, n_valid of them in range):
-// W <- W (1 - lr wd) - lr scale O; optionally O is also stored in fp32.
+// parameter block, n_valid of them in range): W <- W (1 - lr wd) - lr scale O,
+// or W <- O when store_only; O is also stored in fp32 when o is set.
 template <typename TW>
 __device__ __forceinline__ void final_row8(TW* w, float* o, const float (&v)[8], int n_valid, bool vec,
                                            float keep, float step, bool store_only) {
@@ -168,30 +180,31 @@ __device__ __forceinline__ void final_row8(TW* w, float* o, const float (&v)[8],
   }
 }
 
-template <int BM, int BN, typename TI, typename TO, bool RN, bool SYM, int EPI>
+template <int BM, int BN, typename TI, typename TO, bool SYM, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(const GemmArgs a) {
-  constexpr int EPC = Mfma<TI>::EPC;
   constexpr int ES = (int)sizeof(TI);
-  constexpr int BK = 8 * EPC;            // K elements per stage (128 bytes per row)
-  constexpr int WTM = BM / 64;           // 32x32 tiles per wave along M
-  constexpr int WTN = BN / 64;           // ... along N
-  constexpr int WN = BN / 2;             // wave sub-tile width
-  constexpr int NLA = BM * 8 / 256;      // 16-byte chunks of L per thread per stage
-  constexpr int NLB = BN * 8 / 256;      // chunks of R (RT layout)
-  constexpr int NG = BN / EPC;           // column groups of an RN stage
-  constexpr int NBLK = NG * 8;           // EPC x EPC blocks of an RN stage
-  constexpr int NBT = (NBLK + 255) / 256;
-  constexpr int SROW = WN + 8;           // epilogue strip row stride (floats)
-  static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
-  static_assert(!SYM || BM == BN, "symmetric output needs square tiles");
-  static_assert(4 * 32 * SROW * 4 <= 2 * (BM + BN) * 8 * 16, "epilogue staging fits in LDS");
+  constexpr int EPC = 16 / ES;            // elements per 16-byte chunk
+  constexpr int BK = 64 / ES;             // K elements per stage (64 bytes per row)
+  constexpr int NSTG = 4;                 // stages in the LDS ring
+  constexpr int WTM = BM / 64;            // 32x32 tiles per wave along M
+  constexpr int WTN = BN / 64;            // ... along N
+  constexpr int WN = BN / 2;              // wave sub-tile width
+  constexpr int STG = (BM + BN) * 4;      // 16-byte slots per stage
+  constexpr int NQ = STG / 256;           // copy instructions per wave per stage
+  constexpr int NDR = WTM + WTN;          // fragment reads per k16 step
+  constexpr int NPAIR = WTM * WTN;        // fragment pairs per k16 step
+  constexpr int SROW = WN + 8;            // epilogue strip row stride (floats)
+  static_assert(BM == BN, "square tiles");
+  static_assert((BM * 4) % (NQ * 64) == 0, "each wave copies one operand");
+  static_assert(NQ <= NPAIR, "copies fit between the MFMAs of one step");
+  static_assert(4 * 32 * SROW * 4 <= NSTG * STG * 16, "epilogue strips fit in the ring");
 
-  __shared__ u32x4 lds[2][(BM + BN) * 8];
+  __shared__ u32x4 ring[NSTG][STG];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wid = tid >> 6;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: operand choice and buffer resource stay scalar
   const int wm = wid >> 1, wn = wid & 1;
   const int half = lane >> 5;
   const int l32 = lane & 31;
@@ -220,46 +233,31 @@ void gemm_kernel(const GemmArgs a) {
   }
   const int row0 = bi * BM, col0 = bj * BN;
 
-  const TI* Lp = reinterpret_cast<const TI*>(a.L) + (int64_t)unit * a.sL;
-  const TI* Rp = reinterpret_cast<const TI*>(a.R) + (int64_t)unit * a.sR;
-  const __amdgpu_buffer_rsrc_t rL = make_rsrc(Lp, (uint32_t)((int64_t)a.M * a.ldl * ES));
-  const __amdgpu_buffer_rsrc_t rR = make_rsrc(Rp, (uint32_t)((int64_t)(RN ? a.K : a.N) * a.ldr * ES));
+  // ---- copy plan: waves 0,1 copy L rows, waves 2,3 copy R rows.  Copy q of
+  // a wave fills slots [(w * NQ + q) * 64, +64) of the stage; lane l lands in
+  // slot + l, i.e. tile row 16 (w' * NQ + q) + l / 4 and physical chunk
+  // l % 4, which holds logical chunk (l % 4) ^ ((row >> 2) & 3).
+  const bool copiesL = wid < 2;
+  const TI* P = reinterpret_cast<const TI*>(copiesL ? a.L : a.R) +
+                (int64_t)unit * (copiesL ? a.sL : a.sR);
+  const int64_t ld = copiesL ? a.ldl : a.ldr;
+  const int prow0 = copiesL ? row0 : col0;
+  const int prows = copiesL ? a.M : a.N;
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(P, (uint32_t)((int64_t)prows * ld * ES));
+  const int wq = (wid & 1) * NQ;                               // first copy slot-block of this wave
+  const int crow = 16 * wq + (lane >> 2);                      // tile row of copy 0
+  const int cchunk = (lane & 3) ^ ((crow >> 2) & 3);           // same for every copy q
+  const int ck = cchunk * EPC;                                 // k of this lane's chunk in a stage
+  const uint32_t cbase = (uint32_t)(((int64_t)(prow0 + crow) * ld + ck) * ES);
+  const uint32_t cstep = (uint32_t)(16 * ld * ES);
+  const int slot_off = (copiesL ? 0 : BM * 4) + (wid & 1) * NQ * 64;  // first slot of this wave's copies
 
-  // per-thread byte offsets of the stage-0 chunks; a chunk whose row is out
-  // of range (or, in the tail stage, whose first k is) reads as zero
-  uint32_t offL[NLA];
-  int kcL[NLA];  // k of the chunk within a stage
-  bool rowokL[NLA];
-#pragma unroll
-  for (int i = 0; i < NLA; ++i) {
-    const int id = i * 256 + tid;
-    const int r = id >> 3, c = id & 7;
-    rowokL[i] = row0 + r < a.M;
-    offL[i] = rowokL[i] ? (uint32_t)(((int64_t)(row0 + r) * a.ldl + c * EPC) * ES) : 0u;
-    kcL[i] = c * EPC;
-  }
-  uint32_t offR[RN ? NBT : NLB];
-  int kcR[RN ? NBT : NLB];
-  bool okR[RN ? NBT : NLB];
-  if constexpr (!RN) {
-#pragma unroll
-    for (int i = 0; i < NLB; ++i) {
-      const int id = i * 256 + tid;
-      const int r = id >> 3, c = id & 7;
-      okR[i] = col0 + r < a.N;
-      offR[i] = okR[i] ? (uint32_t)(((int64_t)(col0 + r) * a.ldr + c * EPC) * ES) : 0u;
-      kcR[i] = c * EPC;
-    }
-  } else {
-#pragma unroll
-    for (int bt = 0; bt < NBT; ++bt) {
-      const int blk = bt * 256 + tid;
-      const int ng = blk % NG, kg = blk / NG;
-      okR[bt] = blk < NBLK && col0 + ng * EPC < a.N;
-      offR[bt] = okR[bt] ? (uint32_t)(((int64_t)(kg * EPC) * a.ldr + col0 + ng * EPC) * ES) : 0u;
-      kcR[bt] = kg * EPC;
-    }
-  }
+  auto copy_one = [&](int q, int stage) {
+    const int k0 = stage * BK;
+    const bool ok = (k0 + ck < a.K) && (prow0 + crow + 16 * q < prows);
+    const uint32_t off = ok ? cbase + (uint32_t)(k0 * ES) + (uint32_t)q * cstep : OOB;
+    copy16_to_lds(rsrc, &ring[stage % NSTG][slot_off + q * 64], off);
+  };
 
   f32x16 acc[WTM][WTN];
 #pragma unroll
@@ -269,114 +267,69 @@ void gemm_kernel(const GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  u32x4 ra[NLA];
-  u32x4 rb[RN ? NBT * EPC : NLB];
-
-  auto load_stage = [&](int k0) {
-    const bool tail = k0 + BK > a.K;
-#pragma unroll
-    for (int i = 0; i < NLA; ++i) {
-      const bool ok = rowokL[i] && (!tail || k0 + kcL[i] < a.K);
-      ra[i] = bload(rL, ok ? offL[i] + (uint32_t)(k0 * ES) : OOB);
-    }
-    if constexpr (!RN) {
-#pragma unroll
-      for (int i = 0; i < NLB; ++i) {
-        const bool ok = okR[i] && (!tail || k0 + kcR[i] < a.K);
-        rb[i] = bload(rR, ok ? offR[i] + (uint32_t)(k0 * ES) : OOB);
-      }
+  // fragments of one k16 step (16 bytes per lane half), double buffered
+  u32x4 fa[2][WTM], fb[2][WTN];
+  auto read_one = [&](int r, int stage, int s, int slot) {
+    const u32x4* st = ring[stage % NSTG];
+    if (r < WTM) {
+      fa[slot][r] = st[lds_slot4(wm * (BM / 2) + r * 32 + l32, 2 * s + half)];
     } else {
-      const uint32_t kstep = (uint32_t)((int64_t)k0 * a.ldr * ES);
-      const uint32_t rowb = (uint32_t)(a.ldr * ES);
-#pragma unroll
-      for (int bt = 0; bt < NBT; ++bt) {
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          const bool ok = okR[bt] && (!tail || k0 + kcR[bt] + e < a.K);
-          rb[bt * EPC + e] = bload(rR, ok ? offR[bt] + kstep + (uint32_t)e * rowb : OOB);
-        }
-      }
+      const int j = r - WTM;
+      fb[slot][j] = st[BM * 4 + lds_slot4(wn * WN + j * 32 + l32, 2 * s + half)];
     }
   };
-
-  auto store_stage = [&](int buf) {
-    u32x4* sL = lds[buf];
-    u32x4* sR = lds[buf] + BM * 8;
-#pragma unroll
-    for (int i = 0; i < NLA; ++i) {
-      const int id = i * 256 + tid;
-      sL[lds_slot(id >> 3, id & 7)] = ra[i];
-    }
-    if constexpr (!RN) {
-#pragma unroll
-      for (int i = 0; i < NLB; ++i) {
-        const int id = i * 256 + tid;
-        sR[lds_slot(id >> 3, id & 7)] = rb[i];
-      }
-    } else {
-#pragma unroll
-      for (int bt = 0; bt < NBT; ++bt) {
-        const int blk = bt * 256 + tid;
-        if (blk < NBLK) {
-          const int ng = blk % NG, kg = blk / NG;
-          if constexpr (EPC == 8) {
-            u32x4 in[8], out[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) in[e] = rb[bt * 8 + e];
-            transpose8x8_b16(in, out);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) sR[lds_slot(ng * 8 + c, kg)] = out[c];
-          } else {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              u32x4 o;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) o[e] = rb[bt * 4 + e][c];
-              sR[lds_slot(ng * 4 + c, kg)] = o;
-            }
-          }
-        }
-      }
-    }
-  };
-
-  auto compute_stage = [&](int buf) {
-    const u32x4* sL = lds[buf];
-    const u32x4* sR = lds[buf] + BM * 8;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 fa[WTM], fb[WTN];
-#pragma unroll
-      for (int i = 0; i < WTM; ++i) fa[i] = sL[lds_slot(wm * (BM / 2) + i * 32 + l32, 2 * s + half)];
-#pragma unroll
-      for (int j = 0; j < WTN; ++j) fb[j] = sR[lds_slot(wn * WN + j * 32 + l32, 2 * s + half)];
-#pragma unroll
-      for (int i = 0; i < WTM; ++i)
-#pragma unroll
-        for (int j = 0; j < WTN; ++j) Mfma<TI>::run(acc[i][j], fa[i], fb[j]);
-    }
+  auto mfma_pair = [&](int p, int slot) {
+    const int i = p / WTN, j = p % WTN;
+    Mfma<TI>::run(acc[i][j], fa[slot][i], fb[slot][j]);
   };
 
   const int nk = (a.K + BK - 1) / BK;
-  load_stage(0);
-  store_stage(0);
+  // prologue: stages 0 .. NSTG-1 in flight, then stage 0 visible
+#pragma unroll
+  for (int s = 0; s < NSTG; ++s)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) copy_one(q, s);
+  wait_vmcnt<(NSTG - 1) * NQ>();
   __syncthreads();
+#pragma unroll
+  for (int r = 0; r < NDR; ++r) read_one(r, 0, 0, 0);
+
   for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) load_stage((kt + 1) * BK);
-    compute_stage(kt & 1);
-    if (more) store_stage((kt + 1) & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // step 0: MFMAs on slot 0, fragment reads of step 1
+#pragma unroll
+    for (int p = 0; p < NPAIR; ++p) {
+      mfma_pair(p, 0);
+      if (p < NDR) read_one(p, kt, 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // this wave's copies of stage kt+1 landed and its fragment reads of
+    // stage kt are done; after the barrier the same holds for every wave, so
+    // stage kt's slot may be refilled
+    wait_vmcnt_lgkm0<(NSTG - 2) * NQ>();
     __syncthreads();
+    // step 1: MFMAs on slot 1, copies of stage kt+NSTG into the freed slot,
+    // fragment reads of step 0 of stage kt+1
+#pragma unroll
+    for (int p = 0; p < NPAIR; ++p) {
+      mfma_pair(p, 1);
+      if (p < NQ) copy_one(p, kt + NSTG);
+      if (p < NDR) read_one(p, kt + 1, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // ---------------------------------------------------------------- epilogue
+  wait_vmcnt<0>();  // the trailing (zero) copies have landed
+  __syncthreads();                      // every wave is done with the ring
   float alpha = a.alpha;
   if (a.alphaSel != SEL_ONE) {
     const float4 ax = a.aux[unit];
     alpha *= a.alphaSel == SEL_INV_S ? ax.y : ax.z;
   }
   const TI* Ep = reinterpret_cast<const TI*>(a.E) + (int64_t)unit * a.sE;
-  TO* Cp = reinterpret_cast<TO*>(a.C) + (int64_t)unit * a.sC;
+  TO* Cp = a.C ? reinterpret_cast<TO*>(a.C) + (int64_t)unit * a.sC : nullptr;
+  TO* C2p = a.C2 ? reinterpret_cast<TO*>(a.C2) + (int64_t)unit * a.sC2 : nullptr;
 
   float keep = 1.f, step = 0.f;
   UnitDesc d;
@@ -386,8 +339,11 @@ void gemm_kernel(const GemmArgs a) {
     step = a.lr * d.scale;
   }
   const bool diag = SYM && bi == bj;
-  const bool mirror = (SYM) || (EPI == EPI_FINAL && a.tall);
-  float* strip = reinterpret_cast<float*>(&lds[0][0]) + wid * (32 * SROW);
+  // FINAL: the tile is O^T (rows: the unit's n index, columns: its m index);
+  // a tall unit's parameter block has that layout, a wide unit's the transposed one
+  const bool fdirect = EPI == EPI_FINAL && a.tall;
+  const bool fmirror = EPI == EPI_FINAL && !a.tall;
+  float* strip = reinterpret_cast<float*>(&ring[0][0]) + wid * (32 * SROW);
 
 #pragma unroll
   for (int i = 0; i < WTM; ++i) {
@@ -403,25 +359,39 @@ void gemm_kernel(const GemmArgs a) {
     const int gr0 = row0 + wm * (BM / 2) + i * 32;  // global row of strip row 0
     const int gc0 = col0 + wn * WN;                 // global column of strip column 0
 
-    // direct pass: strip row r, columns c8..c8+7
-    if (!(EPI == EPI_FINAL && a.tall)) {
+    // direct pass: output values in place, stored as rows when requested
 #pragma unroll 2
-      for (int t = 0; t < 32 * WN / 8 / 64; ++t) {
-        const int q = t * 64 + lane;
-        const int r = q / (WN / 8), c8 = (q % (WN / 8)) * 8;
-        const int gi = gr0 + r, gj = gc0 + c8;
-        if (gi >= a.M) continue;
-        float v[8];
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(strip + r * SROW + c8);
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(strip + r * SROW + c8 + 4);
+    for (int t = 0; t < 32 * WN / 8 / 64; ++t) {
+      const int q = t * 64 + lane;
+      const int r = q / (WN / 8), c8 = (q % (WN / 8)) * 8;
+      const int gi = gr0 + r, gj = gc0 + c8;
+      float* sp = strip + r * SROW + c8;
+      float v[8];
+      {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(sp);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(sp + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) { v[e] = lo[e]; v[e + 4] = hi[e]; }
-        if constexpr (EPI == EPI_FINAL) {
-          if (gj >= a.N) continue;
-          float e8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-          if (a.beta != 0.f) load8(Ep + (int64_t)gi * a.lde + gj, e8);
+      }
+      const bool inb = gi < a.M && gj < a.N;  // 8-chunks end inside the ld padding
+      if constexpr (EPI == EPI_SCALE) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = alpha * (a.beta * e8[e] + v[e]);
+        for (int e = 0; e < 8; ++e) v[e] *= alpha;
+      } else if constexpr (EPI == EPI_POLY) {
+        float e8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (inb) load8(Ep + (int64_t)gi * a.lde + gj, e8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = alpha * v[e] + a.beta * e8[e] + (gi == gj + e ? a.gamma : 0.f);
+      } else {
+        float e8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (a.beta != 0.f && inb) load8(Ep + (int64_t)gi * a.lde + gj, e8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = alpha * (a.beta * e8[e] + v[e]);
+      }
+      *reinterpret_cast<f32x4*>(sp) = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4*>(sp + 4) = f32x4{v[4], v[5], v[6], v[7]};
+      if constexpr (EPI == EPI_FINAL) {
+        if (fdirect && gi < a.M && gj < a.N) {
           const int64_t off = (int64_t)gi * d.ld + gj;
           const int nv = min(8, a.N - gj);
           float* o = d.o ? d.o + off : nullptr;
@@ -431,27 +401,14 @@ void gemm_kernel(const GemmArgs a) {
           else
             final_row8(reinterpret_cast<float*>(d.w) + off, o, v, nv, a.wvec != 0, keep, step,
                        a.finalMode == FINAL_STORE);
-        } else {
-          if (gj >= a.ldc) continue;
-          if constexpr (EPI == EPI_SCALE) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] *= alpha;
-          } else if constexpr (EPI == EPI_POLY) {
-            float e8[8];
-            load8(Ep + (int64_t)gi * a.lde + gj, e8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = alpha * v[e] + a.beta * e8[e] + (gi == gj + e ? a.gamma : 0.f);
-          } else {
-            float e8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            if (a.beta != 0.f) load8(Ep + (int64_t)gi * a.lde + gj, e8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = alpha * (a.beta * e8[e] + v[e]);
-          }
+        }
+      } else {
+        if (Cp && inb) {
           TO* dst = Cp + (int64_t)gi * a.ldc + gj;
           if (!diag || gi <= gj) {
             store8(dst, v);
           } else if (gi < gj + 8) {
-            // diagonal tile: only the upper triangle (gi <= column) is stored
+            // diagonal tile: the upper triangle (column >= row) is stored
 #pragma unroll
             for (int e = 0; e < 8; ++e)
               if (gi <= gj + e) dst[e] = from_f32<TO>(v[e]);
@@ -460,71 +417,45 @@ void gemm_kernel(const GemmArgs a) {
       }
     }
 
-    // mirror pass: strip column jj, rows c8..c8+7 -> output row gc0 + jj
+    // mirror pass: strip column jj, rows c8..c8+7 -> row gc0 + jj of the
+    // transposed output
+    const bool mirror = EPI == EPI_FINAL ? fmirror : C2p != nullptr;
     if (mirror) {
-      // recompute the epilogue values for the transposed positions: the
-      // symmetric epilogues are symmetric, so the value of (gi, gj) is the
-      // value stored at (gj, gi)
+      __syncthreads();  // values of the direct pass are in the strip
 #pragma unroll 2
       for (int t = 0; t < 32 * WN / 8 / 64; ++t) {
         const int q = t * 64 + lane;
         const int jj = q % WN, c8 = (q / WN) * 8;
-        const int gj = gc0 + jj;       // output row
-        const int gi = gr0 + c8;       // first output column
+        const int gj = gc0 + jj;  // output row
+        const int gi = gr0 + c8;  // first output column
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = strip[(c8 + e) * SROW + jj];
         if constexpr (EPI == EPI_FINAL) {
-          // tall unit: parameter row gj (< n), columns gi.. (< m)
-          if (gj >= a.N || gi >= a.M) continue;
-          float e8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-          if (a.beta != 0.f) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              e8[e] = (gi + e < a.M) ? to_f32(Ep[(int64_t)(gi + e) * a.lde + gj]) : 0.f;
+          // wide unit: parameter row gj (< m, the tile's column index), columns gi.. (< n)
+          if (gj < a.N && gi < a.M) {
+            const int64_t off = (int64_t)gj * d.ld + gi;
+            const int nv = min(8, a.M - gi);
+            float* o = d.o ? d.o + off : nullptr;
+            if (a.wdtype == DT_BF16)
+              final_row8(reinterpret_cast<bf16*>(d.w) + off, o, v, nv, a.wvec != 0, keep, step,
+                         a.finalMode == FINAL_STORE);
+            else
+              final_row8(reinterpret_cast<float*>(d.w) + off, o, v, nv, a.wvec != 0, keep, step,
+                         a.finalMode == FINAL_STORE);
           }
+        } else {
+          // rows of C2 are the tile's columns (< N), its columns the tile's rows
+          if (gj < a.N && gi < a.M) {
+            TO* dst = C2p + (int64_t)gj * a.ldc2 + gi;
+            if (!diag || gi + 7 < gj) {
+              store8(dst, v);
+            } else {
+              // diagonal tile of a symmetric product: strictly lower positions
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = alpha * (a.beta * e8[e] + v[e]);
-          const int64_t off = (int64_t)gj * d.ld + gi;
-          const int nv = min(8, a.M - gi);
-          float* o = d.o ? d.o + off : nullptr;
-          if (a.wdtype == DT_BF16)
-            final_row8(reinterpret_cast<bf16*>(d.w) + off, o, v, nv, a.wvec != 0, keep, step,
-                       a.finalMode == FINAL_STORE);
-          else
-            final_row8(reinterpret_cast<float*>(d.w) + off, o, v, nv, a.wvec != 0, keep, step,
-                       a.finalMode == FINAL_STORE);
-        } else if constexpr (SYM) {
-          if (gj >= a.M || gi >= a.ldc) continue;
-          if (diag && gi + 7 >= gj) {
-            // diagonal tile: lower-triangle positions (column < row) only
-            bool any = false;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) any |= gi + e < gj;
-            if (!any) continue;
-          }
-          if constexpr (EPI == EPI_SCALE) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] *= alpha;
-          } else if constexpr (EPI == EPI_POLY) {
-            // E symmetric: E[gi + e][gj] = E[gj][gi + e]
-            float e8[8];
-            load8(Ep + (int64_t)gj * a.lde + gi, e8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = alpha * v[e] + a.beta * e8[e];
-          } else {
-            float e8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            if (a.beta != 0.f) load8(Ep + (int64_t)gj * a.lde + gi, e8);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = alpha * (a.beta * e8[e] + v[e]);
-          }
-          TO* dst = Cp + (int64_t)gj * a.ldc + gi;
-          if (!diag || gi + 7 < gj) {
-            store8(dst, v);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (gi + e < gj) dst[e] = from_f32<TO>(v[e]);
+              for (int e = 0; e < 8; ++e)
+                if (gi + e < gj) dst[e] = from_f32<TO>(v[e]);
+            }
           }
         }
       }

@@ -5,25 +5,24 @@
 namespace muon {
 
 namespace {
-template <int T, typename TO, bool RN, bool SYM, int EPI>
+template <int T, typename TO, bool SYM, int EPI>
 hipError_t go(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<T, T, float, TO, RN, SYM, EPI>), dim3(a.totalTiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<T, T, float, TO, SYM, EPI>), dim3(a.totalTiles), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 template <int T>
-hipError_t dispatch(int to, bool rn, bool sym, int epi, const GemmArgs& a, hipStream_t s) {
-  if (!rn && sym && epi == EPI_SCALE && to == DT_F32) return go<T, float, false, true, EPI_SCALE>(a, s);
-  if (!rn && sym && epi == EPI_POLY && to == DT_F32) return go<T, float, false, true, EPI_POLY>(a, s);
-  if (!rn && !sym && epi == EPI_AXPY && to == DT_F32) return go<T, float, false, false, EPI_AXPY>(a, s);
-  if (rn && !sym && epi == EPI_AXPY && to == DT_F32) return go<T, float, true, false, EPI_AXPY>(a, s);
-  if (rn && !sym && epi == EPI_FINAL) return go<T, float, true, false, EPI_FINAL>(a, s);
+hipError_t dispatch(int to, bool sym, int epi, const GemmArgs& a, hipStream_t s) {
+  if (sym && epi == EPI_SCALE && to == DT_F32) return go<T, float, true, EPI_SCALE>(a, s);
+  if (sym && epi == EPI_POLY && to == DT_F32) return go<T, float, true, EPI_POLY>(a, s);
+  if (!sym && epi == EPI_AXPY && to == DT_F32) return go<T, float, false, EPI_AXPY>(a, s);
+  if (!sym && epi == EPI_FINAL) return go<T, float, false, EPI_FINAL>(a, s);
   return hipErrorInvalidValue;
 }
 }  // namespace
 
-hipError_t launch_gemm_f32(int tile, int to, bool rn, bool sym, int epi, const GemmArgs& a, hipStream_t s) {
-  return tile == 256 ? dispatch<256>(to, rn, sym, epi, a, s) : dispatch<128>(to, rn, sym, epi, a, s);
+hipError_t launch_gemm_f32(int tile, int to, bool sym, int epi, const GemmArgs& a, hipStream_t s) {
+  return tile == 256 ? dispatch<256>(to, sym, epi, a, s) : dispatch<128>(to, sym, epi, a, s);
 }
 
 }  // namespace muon

@@ -10,12 +10,13 @@ enum : int32_t { SEL_ONE = 0, SEL_INV_S = 1, SEL_INV_S2 = 2 };
 enum : int32_t { FINAL_UPDATE = 0, FINAL_STORE = 1 };
 
 struct GemmArgs {
-  const void* L;
-  const void* R;
-  const void* E;   // epilogue addend (EPI_POLY, EPI_AXPY, EPI_FINAL), same shape as C
-  void* C;
-  int64_t ldl, ldr, lde, ldc;
-  int64_t sL, sR, sE, sC;  // per-unit strides in elements
+  const void* L;   // M x K, K contiguous
+  const void* R;   // N x K, K contiguous
+  const void* E;   // epilogue addend (EPI_POLY, EPI_AXPY), same layout as C
+  void* C;         // direct output (M x N), or null
+  void* C2;        // mirror output (N x M, the transpose), or null; C for a symmetric product
+  int64_t ldl, ldr, lde, ldc, ldc2;
+  int64_t sL, sR, sE, sC, sC2;  // per-unit strides in elements
   int32_t M, N, K;         // logical per-unit sizes
   int32_t units, tilesM, tilesN, tilesPerUnit, totalTiles;
   float alpha, beta, gamma;
@@ -32,9 +33,10 @@ struct GemmArgs {
 // Momentum kernel (see elementwise.hpp).
 struct MomArgs {
   const UnitDesc* desc;
-  void* X0;
-  int64_t ldx;     // leading dimension of X0 (multiple of 8)
-  int64_t sX;      // per-unit element stride of X0
+  void* D;         // U in the parameter's own layout (rows x cols)
+  void* T;         // U transposed (cols x rows)
+  int64_t ldd, ldt;  // leading dimensions (multiples of 8)
+  int64_t sD, sT;    // per-unit element strides
   float* partials; // one per workgroup
   int32_t rows, cols;      // unit shape in parameter layout
   int32_t tilesR, tilesC, tilesPerUnit;

@@ -4,36 +4,25 @@
 
 namespace muon {
 
-hipError_t launch_gemm(int tile, int ti, int to, bool rn, bool sym, int epi, const GemmArgs& a,
-                       hipStream_t s) {
+hipError_t launch_gemm(int tile, int ti, int to, bool sym, int epi, const GemmArgs& a, hipStream_t s) {
   if (a.totalTiles <= 0) return hipSuccess;
   switch (ti) {
-    case DT_BF16: return launch_gemm_bf16(tile, to, rn, sym, epi, a, s);
-    case DT_F16: return launch_gemm_f16(tile, to, rn, sym, epi, a, s);
-    case DT_F32: return launch_gemm_f32(tile, to, rn, sym, epi, a, s);
+    case DT_BF16: return launch_gemm_bf16(tile, to, sym, epi, a, s);
+    case DT_F16: return launch_gemm_f16(tile, to, sym, epi, a, s);
+    case DT_F32: return launch_gemm_f32(tile, to, sym, epi, a, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_momentum(int gdtype, int xdtype, bool tall, const MomArgs& a, int64_t blocks,
+hipError_t launch_momentum(int gdtype, int xdtype, bool /*tall*/, const MomArgs& a, int64_t blocks,
                            hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   const dim3 g((unsigned)blocks), b(256);
-  if (gdtype == DT_BF16 && xdtype == DT_BF16) {
-    if (tall) hipLaunchKernelGGL((momentum_kernel<bf16, bf16, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((momentum_kernel<bf16, bf16, false>), g, b, 0, s, a);
-  } else if (gdtype == DT_F32 && xdtype == DT_F32) {
-    if (tall) hipLaunchKernelGGL((momentum_kernel<float, float, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((momentum_kernel<float, float, false>), g, b, 0, s, a);
-  } else if (gdtype == DT_BF16 && xdtype == DT_F32) {
-    if (tall) hipLaunchKernelGGL((momentum_kernel<bf16, float, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((momentum_kernel<bf16, float, false>), g, b, 0, s, a);
-  } else if (gdtype == DT_F32 && xdtype == DT_BF16) {
-    if (tall) hipLaunchKernelGGL((momentum_kernel<float, bf16, true>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((momentum_kernel<float, bf16, false>), g, b, 0, s, a);
-  } else {
-    return hipErrorInvalidValue;
-  }
+  if (gdtype == DT_BF16 && xdtype == DT_BF16) hipLaunchKernelGGL((momentum_kernel<bf16, bf16>), g, b, 0, s, a);
+  else if (gdtype == DT_F32 && xdtype == DT_F32) hipLaunchKernelGGL((momentum_kernel<float, float>), g, b, 0, s, a);
+  else if (gdtype == DT_BF16 && xdtype == DT_F32) hipLaunchKernelGGL((momentum_kernel<bf16, float>), g, b, 0, s, a);
+  else if (gdtype == DT_F32 && xdtype == DT_BF16) hipLaunchKernelGGL((momentum_kernel<float, bf16>), g, b, 0, s, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -28,7 +28,7 @@ struct PlanBucket {
   int64_t ldx;           // leading dimension of m x n matrices (round_up(n, 8))
   int64_t mp;            // leading dimension of m x m matrices (round_up(m, 8))
   int32_t km_tiles;      // momentum-kernel workgroups per unit
-  size_t off[6];         // data sub-buffers: standard X0 X1 A B; gram X0 R P Q1 Q2 T
+  size_t off[8];         // data sub-buffers: standard X Y0 Y1 A B; gram X0 Y0 R T PZ0 PZ1 PZ2
   size_t data_bytes;     // per chunk
 };
 
