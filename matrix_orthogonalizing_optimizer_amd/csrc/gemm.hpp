@@ -18,24 +18,28 @@
 // built from 32x32 MFMA tiles (v_mfma_f32_32x32x16_{bf16,f16}; fp32 issues
 // four v_mfma_f32_32x32x2_f32 per 16-byte fragment), accumulators in AGPRs.
 //
-// Operand staging: K advances 64 bytes per stage.  Global -> LDS copies use
-// buffer_load_dwordx4 ... lds (each lane's 16 bytes land at M0 + 16 * lane),
-// four stages in flight in an LDS ring, so no registers hold staged data and
-// the wave never stalls on a copy it is about to store.  The lane -> chunk
-// assignment realises an XOR swizzle of the 16-byte chunks of each 64-byte
-// row that keeps the 32-row fragment reads conflict free.  Out-of-range rows
-// and K chunks get an out-of-range buffer offset and read as zero; along K a
-// 16-byte chunk is read when its first element is in range, which relies on
-// leading dimensions that are multiples of 8 with zero padding (the workspace
-// layout guarantees it).  Every operand matrix is smaller than 2^31 bytes
-// (checked by the planner).
+// Operand staging: K advances 128 bytes per row per stage (whole cache
+// lines: the vector L1 keeps a bounded number of line requests in flight, so
+// 128-byte pieces move twice the data of 64-byte ones).  Global -> LDS copies
+// use buffer_load_dwordx4 ... lds (each lane's 16 bytes land at M0 + 16 *
+// lane, 8 rows x 128 bytes per instruction), two stages in an LDS ring, so no
+// registers hold staged data.  The 16-byte chunks of a row are XOR-swizzled
+// with (row & 7) ^ ((row >> 3) & 1), which keeps the 32-row fragment reads
+// free of bank conflicts for 8 and for 16 lanes per LDS cycle.  Out-of-range
+// rows and K chunks get an out-of-range buffer offset and read as zero; along
+// K a 16-byte chunk is read when its first element is in range, which relies
+// on leading dimensions that are multiples of 8 with zero padding (the
+// workspace layout guarantees it).  Every operand matrix is smaller than 2^31
+// bytes (checked by the planner).
 //
-// Schedule per stage (two k16 steps): step 0's MFMAs carry the fragment reads
-// of step 1; a barrier (after this wave's copies of the next stage landed)
-// separates the steps; step 1's MFMAs carry the next-next-next stage's copies
-// into the slot just freed and the fragment reads of the next stage's step 0.
-// A wave issues in order and an MFMA keeps the matrix pipe busy for 32
-// cycles, so each memory instruction is placed between two MFMAs.
+// Schedule per stage (four k-steps of 16 bytes per lane half): the MFMAs of
+// each step carry the fragment reads of the next; before the last step a
+// barrier (after this wave's copies of the next stage landed and its reads
+// of this stage completed) frees this stage's slot; the last step's MFMAs
+// carry the copies of the stage after next into it and the fragment reads of
+// the next stage's first step.  A wave issues in order and an MFMA keeps the
+// matrix pipe busy for 32 cycles, so each memory instruction is placed
+// between two MFMAs.
 //
 // Epilogue: each wave stages its accumulators in LDS one 32-row strip at a
 // time, turns them into output values in place (scale, polynomial, axpy with
@@ -104,11 +108,6 @@ template <int N> __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 // 16 bytes per lane from global memory straight into LDS at dst + 16 * lane.
 __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, off, 0, 0, 0);
-}
-
-// 16-byte slot of (row, chunk) in a stage tile with 4 chunks per 64-byte row.
-__device__ __forceinline__ int lds_slot4(int row, int chunk) {
-  return row * 4 + (chunk ^ ((row >> 2) & 3));
 }
 
 // Upper-triangle tile t (row-major over bi <= bj) of a T x T tile grid.
@@ -185,19 +184,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(const GemmArgs a) {
   constexpr int ES = (int)sizeof(TI);
   constexpr int EPC = 16 / ES;            // elements per 16-byte chunk
-  constexpr int BK = 64 / ES;             // K elements per stage (64 bytes per row)
-  constexpr int NSTG = 4;                 // stages in the LDS ring
+  constexpr int CPR = 8;                  // chunks per row per stage: 128 bytes, whole cache lines
+  constexpr int BK = CPR * EPC;           // K elements per stage
+  constexpr int NSTG = 2;                 // stages in the LDS ring
+  constexpr int NSTEP = CPR / 2;          // MFMA k-steps per stage (one chunk per lane half)
   constexpr int WTM = BM / 64;            // 32x32 tiles per wave along M
   constexpr int WTN = BN / 64;            // ... along N
   constexpr int WN = BN / 2;              // wave sub-tile width
-  constexpr int STG = (BM + BN) * 4;      // 16-byte slots per stage
-  constexpr int NQ = STG / 256;           // copy instructions per wave per stage
-  constexpr int NDR = WTM + WTN;          // fragment reads per k16 step
-  constexpr int NPAIR = WTM * WTN;        // fragment pairs per k16 step
+  constexpr int STG = (BM + BN) * CPR;    // 16-byte slots per stage
+  constexpr int NQ = STG / 256;           // copy instructions per wave per stage (8 rows each)
+  constexpr int NDR = WTM + WTN;          // fragment reads per k-step
+  constexpr int NPAIR = WTM * WTN;        // fragment pairs per k-step
+  constexpr int CPP = (NQ + NPAIR - 1) / NPAIR;  // copies issued per MFMA pair
   constexpr int SROW = WN + 8;            // epilogue strip row stride (floats)
   static_assert(BM == BN, "square tiles");
-  static_assert((BM * 4) % (NQ * 64) == 0, "each wave copies one operand");
-  static_assert(NQ <= NPAIR, "copies fit between the MFMAs of one step");
+  static_assert(NQ * 8 == BM / 2, "each wave copies half of one operand's rows");
+  static_assert(NDR <= NPAIR, "fragment reads fit between the MFMAs of one step");
   static_assert(4 * 32 * SROW * 4 <= NSTG * STG * 16, "epilogue strips fit in the ring");
 
   __shared__ u32x4 ring[NSTG][STG];
@@ -233,29 +235,31 @@ void gemm_kernel(const GemmArgs a) {
   }
   const int row0 = bi * BM, col0 = bj * BN;
 
-  // ---- copy plan: waves 0,1 copy L rows, waves 2,3 copy R rows.  Copy q of
-  // a wave fills slots [(w * NQ + q) * 64, +64) of the stage; lane l lands in
-  // slot + l, i.e. tile row 16 (w' * NQ + q) + l / 4 and physical chunk
-  // l % 4, which holds logical chunk (l % 4) ^ ((row >> 2) & 3).
+  // ---- copy plan: waves 0,1 copy L rows, waves 2,3 copy R rows, each wave
+  // half of its operand's rows.  Copy q of a wave fills 64 consecutive slots
+  // = 8 rows x 8 chunks; lane l lands in row 8q + l/8 (of the wave's half)
+  // at physical chunk l % 8, which holds logical chunk (l % 8) ^ swz(row),
+  // swz(row) = (row & 7) ^ ((row >> 3) & 1) = (l / 8) ^ (q & 1).
   const bool copiesL = wid < 2;
   const TI* P = reinterpret_cast<const TI*>(copiesL ? a.L : a.R) +
                 (int64_t)unit * (copiesL ? a.sL : a.sR);
   const int64_t ld = copiesL ? a.ldl : a.ldr;
-  const int prow0 = copiesL ? row0 : col0;
+  const int crow = (copiesL ? row0 : col0) + (wid & 1) * (BM / 2) + (lane >> 3);  // operand row of copy 0
   const int prows = copiesL ? a.M : a.N;
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(P, (uint32_t)((int64_t)prows * ld * ES));
-  const int wq = (wid & 1) * NQ;                               // first copy slot-block of this wave
-  const int crow = 16 * wq + (lane >> 2);                      // tile row of copy 0
-  const int cchunk = (lane & 3) ^ ((crow >> 2) & 3);           // same for every copy q
-  const int ck = cchunk * EPC;                                 // k of this lane's chunk in a stage
-  const uint32_t cbase = (uint32_t)(((int64_t)(prow0 + crow) * ld + ck) * ES);
-  const uint32_t cstep = (uint32_t)(16 * ld * ES);
-  const int slot_off = (copiesL ? 0 : BM * 4) + (wid & 1) * NQ * 64;  // first slot of this wave's copies
+  const int ck0 = ((lane & 7) ^ (lane >> 3)) * EPC;        // k of this lane's chunk, even copies
+  const int ck1 = ((lane & 7) ^ (lane >> 3) ^ 1) * EPC;    // odd copies
+  const uint32_t cb0 = (uint32_t)(((int64_t)crow * ld + ck0) * ES);
+  const uint32_t cb1 = (uint32_t)(((int64_t)crow * ld + ck1) * ES);
+  const uint32_t cstep = (uint32_t)(8 * ld * ES);
+  const int slot_off = (copiesL ? 0 : BM * CPR) + (wid & 1) * (BM / 2) * CPR;
 
   auto copy_one = [&](int q, int stage) {
     const int k0 = stage * BK;
-    const bool ok = (k0 + ck < a.K) && (prow0 + crow + 16 * q < prows);
-    const uint32_t off = ok ? cbase + (uint32_t)(k0 * ES) + (uint32_t)q * cstep : OOB;
+    const int ck = (q & 1) ? ck1 : ck0;
+    const uint32_t cb = (q & 1) ? cb1 : cb0;
+    const bool ok = (k0 + ck < a.K) && (crow + 8 * q < prows);
+    const uint32_t off = ok ? cb + (uint32_t)(k0 * ES) + (uint32_t)q * cstep : OOB;
     copy16_to_lds(rsrc, &ring[stage % NSTG][slot_off + q * 64], off);
   };
 
@@ -267,15 +271,18 @@ void gemm_kernel(const GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  // fragments of one k16 step (16 bytes per lane half), double buffered
+  // fragments of one k-step (16 bytes per lane half), double buffered; the
+  // fragment rows start at multiples of 32, so swz(row) depends on l32 only
   u32x4 fa[2][WTM], fb[2][WTN];
+  const int rswz = (l32 & 7) ^ ((l32 >> 3) & 1);
   auto read_one = [&](int r, int stage, int s, int slot) {
     const u32x4* st = ring[stage % NSTG];
+    const int c = (2 * s + half) ^ rswz;
     if (r < WTM) {
-      fa[slot][r] = st[lds_slot4(wm * (BM / 2) + r * 32 + l32, 2 * s + half)];
+      fa[slot][r] = st[(wm * (BM / 2) + r * 32 + l32) * CPR + c];
     } else {
       const int j = r - WTM;
-      fb[slot][j] = st[BM * 4 + lds_slot4(wn * WN + j * 32 + l32, 2 * s + half)];
+      fb[slot][j] = st[BM * CPR + (wn * WN + j * 32 + l32) * CPR + c];
     }
   };
   auto mfma_pair = [&](int p, int slot) {
@@ -284,36 +291,41 @@ void gemm_kernel(const GemmArgs a) {
   };
 
   const int nk = (a.K + BK - 1) / BK;
-  // prologue: stages 0 .. NSTG-1 in flight, then stage 0 visible
+  // prologue: stages 0 and 1 in flight, then stage 0 visible
 #pragma unroll
-  for (int s = 0; s < NSTG; ++s)
+  for (int q = 0; q < NQ; ++q) copy_one(q, 0);
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) copy_one(q, s);
-  wait_vmcnt<(NSTG - 1) * NQ>();
+  for (int q = 0; q < NQ; ++q) copy_one(q, 1);
+  wait_vmcnt<NQ>();
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < NDR; ++r) read_one(r, 0, 0, 0);
 
   for (int kt = 0; kt < nk; ++kt) {
     __builtin_amdgcn_sched_barrier(0);
-    // step 0: MFMAs on slot 0, fragment reads of step 1
+    // steps 0 .. NSTEP-2: MFMAs on the fragments in registers, reads of the next step
 #pragma unroll
-    for (int p = 0; p < NPAIR; ++p) {
-      mfma_pair(p, 0);
-      if (p < NDR) read_one(p, kt, 1, 1);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int s = 0; s + 1 < NSTEP; ++s) {
+#pragma unroll
+      for (int p = 0; p < NPAIR; ++p) {
+        mfma_pair(p, s & 1);
+        if (p < NDR) read_one(p, kt, s + 1, (s + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // this wave's copies of stage kt+1 landed and its fragment reads of
     // stage kt are done; after the barrier the same holds for every wave, so
     // stage kt's slot may be refilled
-    wait_vmcnt_lgkm0<(NSTG - 2) * NQ>();
+    wait_vmcnt_lgkm0<0>();
     __syncthreads();
-    // step 1: MFMAs on slot 1, copies of stage kt+NSTG into the freed slot,
-    // fragment reads of step 0 of stage kt+1
+    // last step: copies of stage kt+2 into the freed slot, fragment reads of
+    // step 0 of stage kt+1
 #pragma unroll
     for (int p = 0; p < NPAIR; ++p) {
-      mfma_pair(p, 1);
-      if (p < NQ) copy_one(p, kt + NSTG);
+      mfma_pair(p, (NSTEP - 1) & 1);
+#pragma unroll
+      for (int c = 0; c < CPP; ++c)
+        if (p * CPP + c < NQ) copy_one(p * CPP + c, kt + 2);
       if (p < NDR) read_one(p, kt + 1, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
