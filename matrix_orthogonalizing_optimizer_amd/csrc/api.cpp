@@ -123,7 +123,6 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
     g.wd = cp.wd;
     g.finalMode = cp.final_mode;
     g.tall = b.tall;
-    g.wdtype = pdt;
     g.wvec = cp.wvec;
   };
   // symmetric product L . R^T of m x m output into C (both triangles)
@@ -168,7 +167,7 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
       } else {
         final_args(g);
         HIP_TRY(timed(F_FINAL, mm_n, elems * 2.0 * pes, st,
-                      [&] { return launch_gemm(T, cdt, cdt, false, EPI_FINAL, g, st); }));
+                      [&] { return launch_gemm(T, cdt, pdt, false, EPI_FINAL, g, st); }));
       }
     }
     return MUON_OK;
@@ -244,7 +243,7 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
   g.aux = d_aux;
   final_args(g);
   HIP_TRY(timed(F_FINAL, mm_n, elems * 2.0 * pes, st,
-                [&] { return launch_gemm(T, cdt, cdt, false, EPI_FINAL, g, st); }));
+                [&] { return launch_gemm(T, cdt, pdt, false, EPI_FINAL, g, st); }));
   return MUON_OK;
 }
 

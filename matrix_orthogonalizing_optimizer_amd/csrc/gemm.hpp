@@ -149,32 +149,65 @@ template <typename T> __device__ __forceinline__ void store8(T* p, const float (
   }
 }
 
+// 8 consecutive elements of T held as raw 16-byte words (one for 16-bit T,
+// two for fp32), so that a strip's global loads can all be issued before the
+// first one is used.
+template <typename T> struct Raw8 {
+  u32x4 w[sizeof(T) / 2];
+};
+template <typename T> __device__ __forceinline__ void raw_zero(Raw8<T>& r) {
+#pragma unroll
+  for (int h = 0; h < (int)(sizeof(T) / 2); ++h) r.w[h] = u32x4{0u, 0u, 0u, 0u};
+}
+template <typename T> __device__ __forceinline__ void raw_load8(const T* p, Raw8<T>& r) {
+#pragma unroll
+  for (int h = 0; h < (int)(sizeof(T) / 2); ++h) r.w[h] = reinterpret_cast<const u32x4*>(p)[h];
+}
+template <typename T> __device__ __forceinline__ void raw_unpack8(const Raw8<T>& r, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 w = r.w[0];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = to_f32(__builtin_bit_cast(T, (uint16_t)(w[e >> 1] >> ((e & 1) * 16))));
+  } else {
+    // whole-vector bit casts (a bit cast of one vector element lvalue was
+    // lowered to element 0)
+    const f32x4 lo = __builtin_bit_cast(f32x4, r.w[0]);
+    const f32x4 hi = __builtin_bit_cast(f32x4, r.w[1]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] = lo[e]; v[e + 4] = hi[e]; }
+  }
+}
+
 // Fused parameter update of 8 consecutive parameter elements (one row of the
-// parameter block, n_valid of them in range): W <- W (1 - lr wd) - lr scale O,
-// or W <- O when store_only; O is also stored in fp32 when o is set.
+// parameter block): W <- W (1 - lr wd) - lr scale O, or W <- O when
+// store_only; O is also stored in fp32 when o is set.  final8_vec: all 8 in
+// range, 16-byte aligned, the old W already loaded into raw; final8_tail:
+// n_valid of them, element by element.
 template <typename TW>
-__device__ __forceinline__ void final_row8(TW* w, float* o, const float (&v)[8], int n_valid, bool vec,
+__device__ __forceinline__ void final8_vec(TW* w, float* o, const Raw8<TW>& raw, const float (&v)[8],
                                            float keep, float step, bool store_only) {
-  if (vec && n_valid == 8) {
-    float x[8];
-    if (!store_only) {
-      load8(w, x);
+  float x[8];
+  if (!store_only) {
+    raw_unpack8<TW>(raw, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = x[e] * keep - step * v[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = v[e];
-    }
-    store8(w, x);
-    if (o) store8(o, v);
+    for (int e = 0; e < 8; ++e) x[e] = x[e] * keep - step * v[e];
   } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (e < n_valid) {
-        const float x = store_only ? v[e] : to_f32(w[e]) * keep - step * v[e];
-        w[e] = from_f32<TW>(x);
-        if (o) o[e] = v[e];
-      }
+    for (int e = 0; e < 8; ++e) x[e] = v[e];
+  }
+  store8(w, x);
+  if (o) store8(o, v);
+}
+
+template <typename TW>
+__device__ __forceinline__ void final8_tail(TW* w, float* o, const float (&v)[8], int n_valid, float keep,
+                                            float step, bool store_only) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (e < n_valid) {
+      const float x = store_only ? v[e] : to_f32(w[e]) * keep - step * v[e];
+      w[e] = from_f32<TW>(x);
+      if (o) o[e] = v[e];
     }
   }
 }
@@ -350,15 +383,70 @@ void gemm_kernel(const GemmArgs a) {
     keep = 1.f - a.lr * a.wd;
     step = a.lr * d.scale;
   }
+  const bool store_only = a.finalMode == FINAL_STORE;
   const bool diag = SYM && bi == bj;
   // FINAL: the tile is O^T (rows: the unit's n index, columns: its m index);
   // a tall unit's parameter block has that layout, a wide unit's the transposed one
   const bool fdirect = EPI == EPI_FINAL && a.tall;
   const bool fmirror = EPI == EPI_FINAL && !a.tall;
+  const bool use_e = EPI == EPI_POLY || a.beta != 0.f;  // AXPY and FINAL: beta E + L R^T
+  const bool wpre = EPI == EPI_FINAL && !store_only && a.wvec != 0;
   float* strip = reinterpret_cast<float*>(&ring[0][0]) + wid * (32 * SROW);
+
+  // Each pass covers the 32 x WN strip in NT rounds of 64 lanes x 8 elements:
+  // the direct pass by strip rows (r, c8..c8+7), the mirror pass by strip
+  // columns (c8..c8+7 of column jj).
+  constexpr int NT = 32 * WN / 8 / 64;
+  auto dpos = [&](int t, int& r, int& c8) {
+    const int q = t * 64 + lane;
+    r = q / (WN / 8);
+    c8 = (q % (WN / 8)) * 8;
+  };
+  auto mpos = [&](int t, int& jj, int& c8) {
+    const int q = t * 64 + lane;
+    jj = q % WN;
+    c8 = (q / WN) * 8;
+  };
 
 #pragma unroll
   for (int i = 0; i < WTM; ++i) {
+    const int gr0 = row0 + wm * (BM / 2) + i * 32;  // global row of strip row 0
+    const int gc0 = col0 + wn * WN;                 // global column of strip column 0
+
+    // this strip's global loads go out first: the addend E (direct pass
+    // positions) and, for the fused update, the old parameter values
+    // (positions of the pass that writes them)
+    Raw8<TI> pe[NT];
+    Raw8<TO> pw[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      raw_zero(pe[t]);
+      if constexpr (EPI != EPI_SCALE) {
+        int r, c8;
+        dpos(t, r, c8);
+        const int gi = gr0 + r, gj = gc0 + c8;
+        if (use_e && gi < a.M && gj < a.N) raw_load8(Ep + (int64_t)gi * a.lde + gj, pe[t]);
+      }
+      if constexpr (EPI == EPI_FINAL) {
+        raw_zero(pw[t]);
+        int pr, pc;  // parameter row, first column
+        if (fdirect) {
+          int r, c8;
+          dpos(t, r, c8);
+          pr = gr0 + r;
+          pc = gc0 + c8;
+        } else {
+          int jj, c8;
+          mpos(t, jj, c8);
+          pr = gc0 + jj;
+          pc = gr0 + c8;
+        }
+        const int prow_lim = fdirect ? a.M : a.N, pcol_lim = fdirect ? a.N : a.M;
+        if (wpre && pr < prow_lim && pc + 8 <= pcol_lim)
+          raw_load8(reinterpret_cast<const TO*>(d.w) + (int64_t)pr * d.ld + pc, pw[t]);
+      }
+    }
+
     // accumulators of MFMA row-tile i -> strip[32][WN]
 #pragma unroll
     for (int j = 0; j < WTN; ++j)
@@ -368,14 +456,23 @@ void gemm_kernel(const GemmArgs a) {
         for (int r = 0; r < 4; ++r)
           strip[(g4 * 8 + half * 4 + r) * SROW + j * 32 + l32] = acc[i][j][g4 * 4 + r];
     __syncthreads();
-    const int gr0 = row0 + wm * (BM / 2) + i * 32;  // global row of strip row 0
-    const int gc0 = col0 + wn * WN;                 // global column of strip column 0
+
+    // final parameter update of 8 elements at (pr, pc..): vector form when the
+    // row piece is whole and aligned, else element by element
+    auto final8 = [&](const Raw8<TO>& raw, int pr, int pc, int ncols, const float (&v)[8]) {
+      const int64_t off = (int64_t)pr * d.ld + pc;
+      const int nv = min(8, ncols - pc);
+      float* o = d.o ? d.o + off : nullptr;
+      TO* w = reinterpret_cast<TO*>(d.w) + off;  // FINAL: TO is the parameter dtype
+      if (a.wvec != 0 && nv == 8) final8_vec(w, o, raw, v, keep, step, store_only);
+      else final8_tail(w, o, v, nv, keep, step, store_only);
+    };
 
     // direct pass: output values in place, stored as rows when requested
-#pragma unroll 2
-    for (int t = 0; t < 32 * WN / 8 / 64; ++t) {
-      const int q = t * 64 + lane;
-      const int r = q / (WN / 8), c8 = (q % (WN / 8)) * 8;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      int r, c8;
+      dpos(t, r, c8);
       const int gi = gr0 + r, gj = gc0 + c8;
       float* sp = strip + r * SROW + c8;
       float v[8];
@@ -390,30 +487,20 @@ void gemm_kernel(const GemmArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] *= alpha;
       } else if constexpr (EPI == EPI_POLY) {
-        float e8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (inb) load8(Ep + (int64_t)gi * a.lde + gj, e8);
+        float e8[8];
+        raw_unpack8(pe[t], e8);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = alpha * v[e] + a.beta * e8[e] + (gi == gj + e ? a.gamma : 0.f);
       } else {
-        float e8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (a.beta != 0.f && inb) load8(Ep + (int64_t)gi * a.lde + gj, e8);
+        float e8[8];
+        raw_unpack8(pe[t], e8);
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = alpha * (a.beta * e8[e] + v[e]);
       }
       *reinterpret_cast<f32x4*>(sp) = f32x4{v[0], v[1], v[2], v[3]};
       *reinterpret_cast<f32x4*>(sp + 4) = f32x4{v[4], v[5], v[6], v[7]};
       if constexpr (EPI == EPI_FINAL) {
-        if (fdirect && gi < a.M && gj < a.N) {
-          const int64_t off = (int64_t)gi * d.ld + gj;
-          const int nv = min(8, a.N - gj);
-          float* o = d.o ? d.o + off : nullptr;
-          if (a.wdtype == DT_BF16)
-            final_row8(reinterpret_cast<bf16*>(d.w) + off, o, v, nv, a.wvec != 0, keep, step,
-                       a.finalMode == FINAL_STORE);
-          else
-            final_row8(reinterpret_cast<float*>(d.w) + off, o, v, nv, a.wvec != 0, keep, step,
-                       a.finalMode == FINAL_STORE);
-        }
+        if (fdirect && inb) final8(pw[t], gi, gj, a.N, v);
       } else {
         if (Cp && inb) {
           TO* dst = Cp + (int64_t)gi * a.ldc + gj;
@@ -434,31 +521,20 @@ void gemm_kernel(const GemmArgs a) {
     const bool mirror = EPI == EPI_FINAL ? fmirror : C2p != nullptr;
     if (mirror) {
       __syncthreads();  // values of the direct pass are in the strip
-#pragma unroll 2
-      for (int t = 0; t < 32 * WN / 8 / 64; ++t) {
-        const int q = t * 64 + lane;
-        const int jj = q % WN, c8 = (q / WN) * 8;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        int jj, c8;
+        mpos(t, jj, c8);
         const int gj = gc0 + jj;  // output row
         const int gi = gr0 + c8;  // first output column
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = strip[(c8 + e) * SROW + jj];
-        if constexpr (EPI == EPI_FINAL) {
-          // wide unit: parameter row gj (< m, the tile's column index), columns gi.. (< n)
-          if (gj < a.N && gi < a.M) {
-            const int64_t off = (int64_t)gj * d.ld + gi;
-            const int nv = min(8, a.M - gi);
-            float* o = d.o ? d.o + off : nullptr;
-            if (a.wdtype == DT_BF16)
-              final_row8(reinterpret_cast<bf16*>(d.w) + off, o, v, nv, a.wvec != 0, keep, step,
-                         a.finalMode == FINAL_STORE);
-            else
-              final_row8(reinterpret_cast<float*>(d.w) + off, o, v, nv, a.wvec != 0, keep, step,
-                         a.finalMode == FINAL_STORE);
-          }
-        } else {
-          // rows of C2 are the tile's columns (< N), its columns the tile's rows
-          if (gj < a.N && gi < a.M) {
+        // rows of the output are the tile's columns (< N), its columns the tile's rows
+        if (gj < a.N && gi < a.M) {
+          if constexpr (EPI == EPI_FINAL) {
+            final8(pw[t], gj, gi, a.M, v);  // wide unit: parameter row gj, columns gi..
+          } else {
             TO* dst = C2p + (int64_t)gj * a.ldc2 + gi;
             if (!diag || gi + 7 < gj) {
               store8(dst, v);

@@ -16,7 +16,8 @@ hipError_t dispatch(int to, bool sym, int epi, const GemmArgs& a, hipStream_t s)
   if (sym && epi == EPI_SCALE && to == DT_F32) return go<T, float, true, EPI_SCALE>(a, s);
   if (sym && epi == EPI_POLY && to == DT_F32) return go<T, float, true, EPI_POLY>(a, s);
   if (!sym && epi == EPI_AXPY && to == DT_F32) return go<T, float, false, EPI_AXPY>(a, s);
-  if (!sym && epi == EPI_FINAL) return go<T, float, false, EPI_FINAL>(a, s);
+  if (!sym && epi == EPI_FINAL && to == DT_F32) return go<T, float, false, EPI_FINAL>(a, s);
+  if (!sym && epi == EPI_FINAL && to == DT_BF16) return go<T, bf16, false, EPI_FINAL>(a, s);
   return hipErrorInvalidValue;
 }
 }  // namespace

@@ -13,7 +13,7 @@ struct GemmArgs {
   const void* L;   // M x K, K contiguous
   const void* R;   // N x K, K contiguous
   const void* E;   // epilogue addend (EPI_POLY, EPI_AXPY), same layout as C
-  void* C;         // direct output (M x N), or null
+  void* C;         // direct output (M x N), or null; EPI_FINAL writes the parameters (TO = their dtype)
   void* C2;        // mirror output (N x M, the transpose), or null; C for a symmetric product
   int64_t ldl, ldr, lde, ldc, ldc2;
   int64_t sL, sR, sE, sC, sC2;  // per-unit strides in elements
@@ -26,7 +26,6 @@ struct GemmArgs {
   float lr, wd;            // EPI_FINAL
   int32_t finalMode;       // FINAL_UPDATE or FINAL_STORE
   int32_t tall;            // EPI_FINAL: the unit is the transpose of the parameter block
-  int32_t wdtype;          // EPI_FINAL: DT_F32 or DT_BF16
   int32_t wvec;            // EPI_FINAL: parameter / update_out rows are 16-byte aligned, ld % 8 == 0
 };
 

@@ -149,3 +149,29 @@ def test_non_nesterov_and_zero_gradient_unit():
     assert rel(f64(P[0]) - W0[0], ref["W"][0] - W0[0]) <= 1e-4
     # zero gradient: O = 0, the weight only decays
     assert rel(f64(P[1]), W0[1] * (1 - wl.hp["lr"] * wl.hp["weight_decay"])) <= 1e-6
+
+
+@pytest.mark.parametrize("pdt,ns_dtype", [(0, 1), (1, 0)])
+def test_mixed_precision_parameters(pdt, ns_dtype):
+    """fp32 parameters with bf16 Newton-Schulz (2e-2) and bf16 parameters with
+    fp32 Newton-Schulz (1e-4 on O), a wide and a tall unit each."""
+    print(f"muon_step mixed pdt={pdt} ns_dtype={ns_dtype}", flush=True)
+    d = dev()
+    table = [(0, pdt, 512, 1536, 0, 0), (0, pdt, 1536, 512, 0, 0)]
+    wl = configs.Workload("mixed", table, ["wide", "tall"], rank=8, hp=configs._hp())
+    P, M, EA, ES = _state(wl, d)
+    G = gen.make_grads(wl, 0, "cpu")
+    W0 = [f64(p) for p in P]
+    outs = [torch.zeros(r[2], r[3], dtype=torch.float32, device=d) for r in table]
+    StepRunner(table, ns_dtype=ns_dtype, device=d).step(P, [g.to(d) for g in G], M, EA, ES,
+                                                       hp_from(wl.hp), update_outs=outs)
+    torch.cuda.synchronize()
+    ref = oracle.muon_step(table, W0, [f64(g) for g in G], [np.zeros((r[2], r[3])) for r in table],
+                           [None, None], [None, None], _oracle_hp(wl.hp), want_updates=True)
+    tol_o = 2e-2 if ns_dtype == 1 else 1e-4
+    for i in range(2):
+        assert rel(f64(outs[i]), ref["O"][i]) <= tol_o, (i, rel(f64(outs[i]), ref["O"][i]))
+        w_ref = ref["W"][i] if pdt == 0 else stored(ref["W"][i], torch.bfloat16)
+        tol_w = tol_o if pdt == 0 else 2e-2
+        assert rel(f64(P[i]) - W0[i], w_ref - W0[i]) <= tol_w
+        assert rel(f64(M[i]), ref["M"][i]) <= 1e-6
