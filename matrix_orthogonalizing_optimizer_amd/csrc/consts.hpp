@@ -2,7 +2,7 @@
 #pragma once
 
 namespace muon {
-constexpr int KM_TR = 32;       // momentum kernel tile rows (parameter layout)
-constexpr int KM_TC = 128;      // momentum kernel tile columns
+constexpr int KM_TR = 64;       // momentum kernel tile rows (parameter layout)
+constexpr int KM_TC = 64;       // momentum kernel tile columns
 constexpr int ADAM_EPB = 4096;  // AdamW elements per workgroup
 }  // namespace muon

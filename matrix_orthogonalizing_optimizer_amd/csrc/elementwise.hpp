@@ -12,15 +12,45 @@ namespace muon {
 // K-M: momentum / Nesterov + sum of squares.
 // [Blog] "Formulation of Muon Optimizer": M_t = mu M_{t-1} + G_t;
 // "Variation of Muon Optimizer": Nesterov orthogonalizes mu M_t + G_t.
-// One workgroup handles a 32 x 128 tile of one unit (parameter layout).  The
-// unit is written to the workspace X0 as a row-major m x n matrix with
-// leading dimension ldx (zero padded): as is for a wide unit, transposed
-// through LDS for a tall one, so every later GEMM sees a wide operand.
-// Each workgroup writes one partial sum of U^2 (fp32, fixed order).
+// One workgroup handles a 64 x 64 tile of one unit (parameter layout) and
+// writes U in both working layouts: as is (D, leading dimension ldd) and
+// transposed through LDS (T, leading dimension ldt), pad columns zero.  A
+// 64-element row of 16-bit values is one 128-byte line, so every load and
+// store of the tile moves whole lines.  Each workgroup writes one partial sum
+// of U^2 (fp32, fixed order).
 // ---------------------------------------------------------------------------
+
+// 8 elements of T from p, 16-byte aligned (32 for fp32)
+template <typename T> __device__ __forceinline__ void ld8(const T* p, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = to_f32(__builtin_bit_cast(T, (uint16_t)(w[e >> 1] >> ((e & 1) * 16))));
+  } else {
+    const f32x4 lo = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    const f32x4 hi = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] = lo[e]; v[e + 4] = hi[e]; }
+  }
+}
+
+// streaming stores: the data is not read again by this kernel
+template <typename T> __device__ __forceinline__ void st8(T* p, const float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)bits16(from_f32<T>(v[2 * j])) | ((uint32_t)bits16(from_f32<T>(v[2 * j + 1])) << 16);
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+  } else {
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(p));
+    __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(p + 4));
+  }
+}
 
 template <typename TG, typename TX>
 __global__ __launch_bounds__(256) void momentum_kernel(const MomArgs a) {
+  static_assert(KM_TR == 64 && KM_TC == 64, "tile shape");
   __shared__ float tile[KM_TR][KM_TC + 1];
   __shared__ float red[4];
   const int unit = blockIdx.x / a.tilesPerUnit;
@@ -34,112 +64,82 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MomArgs a) {
   TX* __restrict__ XT = reinterpret_cast<TX*>(a.T) + (int64_t)unit * a.sT;
 
   const int tid = threadIdx.x;
-  const int cg = tid & 15;   // 8-column group
-  const int rr = tid >> 4;   // 0..15
+  const int cg = tid & 7;   // 8-column group
+  const int rr = tid >> 3;  // rows rr and rr + 32
+  const int c = c0 + cg * 8;
+  const bool cin = c < a.cols;
+  const bool full = a.vec_ok && c + 8 <= a.cols;
+
+  // loads of both rows first
+  float g[2][8], m[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = r0 + rr + 32 * h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { g[h][e] = 0.f; m[h][e] = 0.f; }
+    if (r < a.rows && cin) {
+      const int64_t off = (int64_t)r * d.ld + c;
+      if (full) {
+        ld8(G + off, g[h]);
+        if (M) ld8(M + off, m[h]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (c + e < a.cols) {
+            g[h][e] = to_f32(G[off + e]);
+            if (M) m[h][e] = M[off + e];
+          }
+        }
+      }
+    }
+  }
+
   float ss = 0.f;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int lr = rr + 16 * h;
+    const int lr = rr + 32 * h;
     const int r = r0 + lr;
-    const int c = c0 + cg * 8;
     float u[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) u[e] = 0.f;
-    if (r < a.rows && c < a.cols) {
-      const int64_t off = (int64_t)r * d.ld + c;
-      float g[8], m[8];
-      const bool full = a.vec_ok && (c + 8 <= a.cols);
-      if (full) {
-        if constexpr (sizeof(TG) == 2) {
-          u32x4 raw = *reinterpret_cast<const u32x4*>(G + off);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            g[e] = to_f32(__builtin_bit_cast(TG, (uint16_t)(raw[e >> 1] >> ((e & 1) * 16))));
-        } else {
-          f32x4 g0 = *reinterpret_cast<const f32x4*>(G + off);
-          f32x4 g1 = *reinterpret_cast<const f32x4*>(G + off + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { g[e] = g0[e]; g[e + 4] = g1[e]; }
-        }
-        if (M) {
-          f32x4 m0 = *reinterpret_cast<const f32x4*>(M + off);
-          f32x4 m1 = *reinterpret_cast<const f32x4*>(M + off + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { m[e] = m0[e]; m[e + 4] = m1[e]; }
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const bool in = c + e < a.cols;
-          g[e] = in ? to_f32(G[off + e]) : 0.f;
-          m[e] = (in && M) ? M[off + e] : 0.f;
-        }
-      }
+    for (int e = 0; e < 8; ++e) {
       if (M) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float mn = fmaf(a.mu, m[e], g[e]);
-          m[e] = mn;
-          u[e] = a.nesterov ? fmaf(a.mu, mn, g[e]) : mn;
-        }
+        const float mn = fmaf(a.mu, m[h][e], g[h][e]);
+        m[h][e] = mn;
+        u[e] = a.nesterov ? fmaf(a.mu, mn, g[h][e]) : mn;
+      } else {
+        u[e] = g[h][e];
+      }
+      ss = fmaf(u[e], u[e], ss);
+    }
+    if (r < a.rows && cin) {
+      const int64_t off = (int64_t)r * d.ld + c;
+      if (M) {
         if (full) {
-          *reinterpret_cast<f32x4*>(M + off) = f32x4{m[0], m[1], m[2], m[3]};
-          *reinterpret_cast<f32x4*>(M + off + 4) = f32x4{m[4], m[5], m[6], m[7]};
+          st8(M + off, m[h]);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (c + e < a.cols) M[off + e] = m[e];
+            if (c + e < a.cols) M[off + e] = m[h][e];
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) u[e] = g[e];
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss = fmaf(u[e], u[e], ss);
-    }
-    // own layout: row r, columns c..c+8 (columns past cols are zero padding)
-    if (r < a.rows && c < a.cols) {
-      TX* dst = X + (int64_t)r * a.ldd + c;
-      if constexpr (sizeof(TX) == 2) {
-        u32x4 p;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          p[j] = (uint32_t)bits16(from_f32<TX>(u[2 * j])) |
-                 ((uint32_t)bits16(from_f32<TX>(u[2 * j + 1])) << 16);
-        *reinterpret_cast<u32x4*>(dst) = p;
-      } else {
-        *reinterpret_cast<f32x4*>(dst) = f32x4{u[0], u[1], u[2], u[3]};
-        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{u[4], u[5], u[6], u[7]};
-      }
+      // own layout: row r, columns c..c+8 (columns past cols are zero padding)
+      st8(X + (int64_t)r * a.ldd + c, u);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) tile[lr][cg * 8 + e] = u[e];
   }
-  {
-    __syncthreads();
-    // transposed layout: row (c0 + c), columns r0 .. r0+32: 128 rows x 4 chunks of 8
+  __syncthreads();
+  // transposed layout: row c0 + cc, columns r0 .. r0+64: 64 rows x 8 chunks of 8
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int q = tid + 256 * j;
-      const int c = q >> 2, rq = q & 3;
-      const int gc = c0 + c, gr = r0 + rq * 8;
-      if (gc < a.cols && gr < a.rows) {
-        TX* dst = XT + (int64_t)gc * a.ldt + gr;
-        float u[8];
+  for (int j = 0; j < 2; ++j) {
+    const int q = tid + 256 * j;
+    const int cc = q >> 3, rq = q & 7;
+    const int gc = c0 + cc, gr = r0 + rq * 8;
+    if (gc < a.cols && gr < a.rows) {
+      float u[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) u[e] = tile[rq * 8 + e][c];
-        if constexpr (sizeof(TX) == 2) {
-          u32x4 p;
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            p[k] = (uint32_t)bits16(from_f32<TX>(u[2 * k])) |
-                   ((uint32_t)bits16(from_f32<TX>(u[2 * k + 1])) << 16);
-          *reinterpret_cast<u32x4*>(dst) = p;
-        } else {
-          *reinterpret_cast<f32x4*>(dst) = f32x4{u[0], u[1], u[2], u[3]};
-          *reinterpret_cast<f32x4*>(dst + 4) = f32x4{u[4], u[5], u[6], u[7]};
-        }
-      }
+      for (int e = 0; e < 8; ++e) u[e] = tile[rq * 8 + e][cc];
+      st8(XT + (int64_t)gc * a.ldt + gr, u);
     }
   }
   const float s = block_sum_256(ss, red);
@@ -179,6 +179,51 @@ __device__ __forceinline__ void adam_elem(float& w, float g, float& m, float& v,
   w = w * a.keep - a.step * (m / (a.eps + sqrtf(v)));
 }
 
+template <typename TW>
+__device__ __forceinline__ void adamw_tile(const AdamDesc& d, int64_t base, const AdamArgs& a) {
+  constexpr int NCH = ADAM_EPB / (256 * 8);  // 8-element chunks per thread
+  TW* __restrict__ W = reinterpret_cast<TW*>(d.w);
+  const TW* __restrict__ G = reinterpret_cast<const TW*>(d.g);
+  int64_t i0[NCH];
+  bool vec[NCH];
+#pragma unroll
+  for (int it = 0; it < NCH; ++it) {
+    i0[it] = base + (int64_t)(it * 256 + threadIdx.x) * 8;
+    vec[it] = d.vec_ok && i0[it] + 8 <= d.numel;
+  }
+  // every load of the tile is issued before the first use
+  float w[NCH][8], g[NCH][8], m[NCH][8], v[NCH][8];
+#pragma unroll
+  for (int it = 0; it < NCH; ++it) {
+    if (vec[it]) {
+      ld8(W + i0[it], w[it]);
+      ld8(G + i0[it], g[it]);
+      ld8(d.m + i0[it], m[it]);
+      ld8(d.v + i0[it], v[it]);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < NCH; ++it) {
+    if (vec[it]) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) adam_elem(w[it][e], g[it][e], m[it][e], v[it][e], a);
+      st8(W + i0[it], w[it]);
+      st8(d.m + i0[it], m[it]);
+      st8(d.v + i0[it], v[it]);
+    } else {
+      for (int e = 0; e < 8; ++e) {
+        const int64_t i = i0[it] + e;
+        if (i >= d.numel) break;
+        float wi = to_f32(W[i]), gi = to_f32(G[i]), mi = d.m[i], vi = d.v[i];
+        adam_elem(wi, gi, mi, vi, a);
+        d.m[i] = mi;
+        d.v[i] = vi;
+        W[i] = from_f32<TW>(wi);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void adamw_kernel(const AdamArgs a) {
   // find the parameter owning this workgroup (binary search over block0)
   int lo = 0, hi = a.nparams - 1;
@@ -190,68 +235,8 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamArgs a) {
   }
   const AdamDesc d = a.desc[lo];
   const int64_t base = (b - d.block0) * ADAM_EPB;
-  for (int it = 0; it < ADAM_EPB / (256 * 8); ++it) {
-    const int64_t i0 = base + (int64_t)(it * 256 + threadIdx.x) * 8;
-    if (i0 >= d.numel) break;
-    if (d.vec_ok && i0 + 8 <= d.numel) {
-      float w[8], g[8], m[8], v[8];
-      f32x4 m0 = *reinterpret_cast<const f32x4*>(d.m + i0), m1 = *reinterpret_cast<const f32x4*>(d.m + i0 + 4);
-      f32x4 v0 = *reinterpret_cast<const f32x4*>(d.v + i0), v1 = *reinterpret_cast<const f32x4*>(d.v + i0 + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { m[e] = m0[e]; m[e + 4] = m1[e]; v[e] = v0[e]; v[e + 4] = v1[e]; }
-      if (d.dtype == DT_BF16) {
-        u32x4 wr = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16*>(d.w) + i0);
-        u32x4 gr = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16*>(d.g) + i0);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          w[e] = to_f32(__builtin_bit_cast(bf16, (uint16_t)(wr[e >> 1] >> ((e & 1) * 16))));
-          g[e] = to_f32(__builtin_bit_cast(bf16, (uint16_t)(gr[e >> 1] >> ((e & 1) * 16))));
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) adam_elem(w[e], g[e], m[e], v[e], a);
-        u32x4 wo;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          wo[j] = (uint32_t)bits16(from_f32<bf16>(w[2 * j])) | ((uint32_t)bits16(from_f32<bf16>(w[2 * j + 1])) << 16);
-        *reinterpret_cast<u32x4*>(reinterpret_cast<bf16*>(d.w) + i0) = wo;
-      } else {
-        const float* wp = reinterpret_cast<const float*>(d.w) + i0;
-        const float* gp = reinterpret_cast<const float*>(d.g) + i0;
-        f32x4 w0 = *reinterpret_cast<const f32x4*>(wp), w1 = *reinterpret_cast<const f32x4*>(wp + 4);
-        f32x4 g0 = *reinterpret_cast<const f32x4*>(gp), g1 = *reinterpret_cast<const f32x4*>(gp + 4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { w[e] = w0[e]; w[e + 4] = w1[e]; g[e] = g0[e]; g[e + 4] = g1[e]; }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) adam_elem(w[e], g[e], m[e], v[e], a);
-        float* wq = reinterpret_cast<float*>(d.w) + i0;
-        *reinterpret_cast<f32x4*>(wq) = f32x4{w[0], w[1], w[2], w[3]};
-        *reinterpret_cast<f32x4*>(wq + 4) = f32x4{w[4], w[5], w[6], w[7]};
-      }
-      *reinterpret_cast<f32x4*>(d.m + i0) = f32x4{m[0], m[1], m[2], m[3]};
-      *reinterpret_cast<f32x4*>(d.m + i0 + 4) = f32x4{m[4], m[5], m[6], m[7]};
-      *reinterpret_cast<f32x4*>(d.v + i0) = f32x4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<f32x4*>(d.v + i0 + 4) = f32x4{v[4], v[5], v[6], v[7]};
-    } else {
-      for (int e = 0; e < 8; ++e) {
-        const int64_t i = i0 + e;
-        if (i >= d.numel) break;
-        float w, g;
-        if (d.dtype == DT_BF16) {
-          w = to_f32(reinterpret_cast<const bf16*>(d.w)[i]);
-          g = to_f32(reinterpret_cast<const bf16*>(d.g)[i]);
-        } else {
-          w = reinterpret_cast<const float*>(d.w)[i];
-          g = reinterpret_cast<const float*>(d.g)[i];
-        }
-        float m = d.m[i], v = d.v[i];
-        adam_elem(w, g, m, v, a);
-        d.m[i] = m;
-        d.v[i] = v;
-        if (d.dtype == DT_BF16) reinterpret_cast<bf16*>(d.w)[i] = from_f32<bf16>(w);
-        else reinterpret_cast<float*>(d.w)[i] = w;
-      }
-    }
-  }
+  if (d.dtype == DT_BF16) adamw_tile<bf16>(d, base, a);
+  else adamw_tile<float>(d, base, a);
 }
 
 }  // namespace muon
