@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default="llama3_8b_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample", default="1024x4096,4096x4096",
+    p.add_argument("--cpu-sample", default=",".join(["1024x4096"] * 8),
                    help="unit shapes the oracle is timed on")
     return p.parse_args()
 
@@ -122,6 +122,12 @@ def main():
                 "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
                 "flops_per_launch": d["flops"] / d["launches"],
                 "avg_launch_ms": d["total_ms"] / d["launches"], "traffic": None}
+    if dom == "ns_update_aX_BX" and wl.method == "standard":
+        # algorithmic HBM bytes of the update GEMM: read Y and B, write Y' and X'
+        es = 2 if table[0][1] == 1 else 4
+        per_step = sum(es * (3.0 * m * n + 1.0 * m * m) for m, n in unit_shapes(table))
+        roofline["algorithmic_bytes_per_launch"] = (wl.hp["ns_steps"] - 1) * per_step * args.steps / d["launches"]
+        roofline["traffic"] = measured_traffic(wl.name)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -155,41 +161,97 @@ def main():
     print(json.dumps(out))
 
 
+def unit_shapes(table):
+    """(m, n) of every Muon unit, m <= n."""
+    out = []
+    for kind, _dt, rows, cols, split, _sd in table:
+        if kind != 0 or rows == 0 or cols == 0:
+            continue
+        h = split if split > 0 else rows
+        out += [(min(h, cols), max(h, cols))] * (rows // h)
+    return out
+
+
+GEMM_SOURCES = ("matrix_orthogonalizing_optimizer_amd/csrc/gemm.hpp",
+                "matrix_orthogonalizing_optimizer_amd/csrc/gemm_bf16.hip")
+
+
+def gemm_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the update GEMM from the committed rocprofv3
+    counter summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's
+    readings), or None when the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_update_gemm_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.startswith("- `"):
+                k, v = line[3:].split("`", 1)
+                vals[k] = v.split(":", 1)[1].strip()
+    if vals.get("kernel_source_sha256") != gemm_source_digest():
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(sample: str, wl, table):
     """The fp64 oracle as it stands, timed on this host on a bounded sample:
     one full Muon unit update (momentum, Newton-Schulz, scaled update) per
-    listed unit shape, with the workload's gradient generator.  Reported as
+    listed unit shape, with the workload's gradient generator.  The plain C++
+    reference (std::thread over all host cores) is the baseline; the numpy
+    reference (BLAS matmul) is timed beside it for context.  Reported as
     nominal Newton-Schulz TFLOP/s, the metric's unit."""
     import numpy as np
     import torch
 
     import oracle
-    from workloads import gen
+    from oracle import cref
+    from workloads import configs, gen
+
+    hp = wl.hp
+    shapes = [tuple(int(x) for x in s.split("x")) for s in sample.split(",")]
+    grads = [gen.lowrank_gradient(r, c, wl.rank, 99 + i, "cpu", torch.float64).to(torch.bfloat16).double().numpy()
+             for i, (r, c) in enumerate(shapes)]
+    flops = sum(hp["ns_steps"] * (4.0 * min(r, c) ** 2 * max(r, c) + 2.0 * min(r, c) ** 3) for r, c in shapes)
+    step_flops = hp["ns_steps"] * configs.ns_flops(table)
+
+    # plain C++ reference
+    t = time.perf_counter()
+    for (r, c), G in zip(shapes, grads):
+        _, U = cref.momentum(np.zeros((r, c)), G, hp["momentum"], hp["nesterov"])
+        O = cref.orthogonalize(U, hp["ns_steps"])
+        cref.weight_update(np.zeros((r, c)), O, hp["lr"], hp["weight_decay"], cref.muon_scale(r, c))
+    secs = time.perf_counter() - t
+    rate = flops / secs / 1e12
+
+    # numpy reference
+    ohp = oracle.OracleHparams(**{k: v for k, v in hp.items() if k in oracle.OracleHparams.__annotations__})
+    t = time.perf_counter()
+    for (r, c), G in zip(shapes, grads):
+        oracle.muon_step([(0, 1, r, c, 0, 0)], [np.zeros((r, c))], [G], [np.zeros((r, c))], [None], [None], ohp)
+    nsecs = time.perf_counter() - t
     try:
         from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        ncores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
-        cores = os.cpu_count() or 1
-    flops = 0.0
-    secs = 0.0
-    shapes = []
-    for s in sample.split(","):
-        r, c = (int(x) for x in s.split("x"))
-        G = gen.lowrank_gradient(r, c, wl.rank, 99, "cpu", torch.float64).to(torch.bfloat16).double().numpy()
-        W = np.zeros((r, c))
-        hp = oracle.OracleHparams(**{k: v for k, v in wl.hp.items() if k in oracle.OracleHparams.__annotations__})
-        t = time.perf_counter()
-        oracle.muon_step([(0, 1, r, c, 0, 0)], [W], [G], [np.zeros((r, c))], [None], [None], hp)
-        secs += time.perf_counter() - t
-        m, n = min(r, c), max(r, c)
-        flops += wl.hp["ns_steps"] * (4.0 * m * m * n + 2.0 * m ** 3)
-        shapes.append(f"{r}x{c}")
-    rate = flops / secs / 1e12
-    step_flops = wl.hp["ns_steps"] * __import__("workloads").configs.ns_flops(table)
-    return {"value": rate, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"one Muon unit update per shape {','.join(shapes)} of the workload "
-                      f"({flops / 1e12:.2f} TFLOP nominal, {secs:.1f} s)",
-            "extrapolated_ms_per_step": 1e3 * step_flops / (rate * 1e12)}
+        ncores = os.cpu_count() or 1
+    label = ",".join(f"{r}x{c}" for r, c in shapes)
+    return {"value": rate, "unit": "TFLOP/s", "cores": cref.threads(), "kind": "oracle",
+            "sample": f"plain C++ fp64 reference, one Muon unit update (momentum, Newton-Schulz, "
+                      f"scaled update) per unit shape {label} of the workload "
+                      f"({flops / 1e12:.3f} TFLOP nominal, {secs:.1f} s)",
+            "extrapolated_ms_per_step": 1e3 * step_flops / (rate * 1e12),
+            "numpy_oracle": {"value": flops / nsecs / 1e12, "unit": "TFLOP/s", "cores": ncores,
+                             "seconds": nsecs}}
 
 
 if __name__ == "__main__":

@@ -1,0 +1,139 @@
+"""ctypes binding of the plain C++ fp64 reference (oracle/muon_ref.cpp).
+
+TEST INFRASTRUCTURE ONLY, like the rest of ``oracle``: loaded by the test
+suite, the smoke check and the benchmark's CPU-baseline leg, never by the
+product path.  ``build()`` compiles the library with g++ (no GPU, no HIP)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "muon_ref.cpp")
+LIB = os.path.join(HERE, "libmuonref.so")
+
+_lib = None
+_D = ctypes.POINTER(ctypes.c_double)
+
+
+def build() -> str:
+    tmp = LIB + ".tmp"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-pthread", "-Wall", SRC, "-o", tmp],
+                   check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            raise RuntimeError(f"{LIB} is not built: run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB)
+        L.ref_set_threads.argtypes = [ctypes.c_int32]
+        L.ref_threads.restype = ctypes.c_int32
+        L.ref_momentum.argtypes = [_D, _D, ctypes.c_int64, ctypes.c_double, ctypes.c_int32, _D]
+        L.ref_orthogonalize.argtypes = [_D, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, _D,
+                                        ctypes.c_int32, _D]
+        L.ref_orthogonalize.restype = ctypes.c_int32
+        L.ref_muon_scale.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double]
+        L.ref_muon_scale.restype = ctypes.c_double
+        L.ref_weight_update.argtypes = [_D, _D, ctypes.c_int64, ctypes.c_double, ctypes.c_double,
+                                        ctypes.c_double]
+        L.ref_adamw.argtypes = [_D, _D, _D, _D, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                                ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double]
+        L.ref_plan.argtypes = [ctypes.POINTER(ctypes.c_int64), ctypes.c_int32, ctypes.c_int32,
+                               ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
+                               ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                               ctypes.POINTER(ctypes.c_int32)]
+        L.ref_plan.restype = ctypes.c_int64
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(_D)
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def set_threads(n: int) -> None:
+    lib().ref_set_threads(int(n))
+
+
+def threads() -> int:
+    return int(lib().ref_threads())
+
+
+def momentum(M, G, mu: float, nesterov: bool):
+    """Returns (M_new, U)."""
+    M = _f64(M).copy()
+    G = _f64(G)
+    U = np.empty_like(M)
+    lib().ref_momentum(_p(M), _p(G), M.size, mu, 1 if nesterov else 0, _p(U))
+    return M, U
+
+
+def orthogonalize(G, steps: int = 5, coeffs: Optional[Sequence] = None, method: str = "standard"):
+    G = _f64(G)
+    rows, cols = G.shape
+    c = None
+    if coeffs is not None:
+        c = _f64(coeffs)
+        if c.shape == (3,):
+            c = np.tile(c, (steps, 1))
+        if c.shape != (steps, 3):
+            raise ValueError("coeffs must be (3,) or (steps, 3)")
+        c = np.ascontiguousarray(c)
+    if method not in ("standard", "gram"):
+        raise ValueError(f"unknown ns method {method!r}")
+    O = np.empty_like(G)
+    st = lib().ref_orthogonalize(_p(G), rows, cols, steps, _p(c) if c is not None else None,
+                                 {"standard": 0, "gram": 1}[method], _p(O))
+    if st != 0:
+        raise ValueError("ref_orthogonalize rejected its arguments")
+    return O
+
+
+def muon_scale(rows: int, cols: int, scale_dim: int = 0, rms_scale: float = 0.2) -> float:
+    return float(lib().ref_muon_scale(rows, cols, scale_dim, rms_scale))
+
+
+def weight_update(W, O, lr: float, wd: float, scale: float):
+    W = _f64(W).copy()
+    O = _f64(O)
+    lib().ref_weight_update(_p(W), _p(O), W.size, lr, wd, scale)
+    return W
+
+
+def adamw(W, g, m, v, t: int, lr: float, b1: float, b2: float, eps: float, wd: float):
+    W, m, v = _f64(W).copy(), _f64(m).copy(), _f64(v).copy()
+    g = _f64(g)
+    lib().ref_adamw(_p(W), _p(g), _p(m), _p(v), W.size, t, lr, b1, b2, eps, wd)
+    return W, m, v
+
+
+def plan(table, method: int = 0, ns_dtype: int = -1):
+    """(units: list of 6-tuples, buckets: list of 8-tuples), both bucket-ordered."""
+    t = np.ascontiguousarray(np.asarray(table, dtype=np.int64).reshape(-1, 6))
+    cap = int(sum(max(1, r[2] // r[4]) if r[4] > 0 else 1 for r in t.tolist())) + 1
+    units = np.zeros((cap, 6), dtype=np.int64)
+    buckets = np.zeros((cap, 8), dtype=np.int32)
+    nb = ctypes.c_int32(0)
+    nu = lib().ref_plan(t.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), len(t), method, ns_dtype,
+                        units.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), cap,
+                        buckets.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), cap, ctypes.byref(nb))
+    if nu < 0:
+        raise RuntimeError("ref_plan capacity")
+    return [tuple(u) for u in units[:nu].tolist()], [tuple(b) for b in buckets[:nb.value].tolist()]
+
+
+# the numpy reference's names, so tests can run the same pins on both
+momentum_update = momentum
+adamw_update = adamw

@@ -9,6 +9,7 @@ import re
 import pytest
 
 import oracle
+from oracle import cref
 from workloads import configs
 
 mo = pytest.importorskip("matrix_orthogonalizing_optimizer_amd")
@@ -70,6 +71,10 @@ def test_plan_matches_oracle_bit_exact(name, ns_dtype):
             exp_u.append((u.param, u.row0, u.rows, u.cols, int(u.tall),
                           u.scale_dim if u.scale_dim > 0 else max(u.rows, u.cols)))
     assert mo.muon_plan_units(plan) == exp_u
+    # the C++ reference's planner, written separately, agrees bit for bit
+    c_units, c_buckets = cref.plan(wl.table, method, ns_dtype)
+    assert c_buckets == exp_b
+    assert c_units == exp_u
     ws = mo.muon_plan_workspace_bytes(plan)
     assert ws > 0
 

@@ -1,7 +1,9 @@
 """Pins of the oracle's orthogonalization against what the mathematics fixes:
 the SVD closed form of the iteration, hand-reduced and rank-1 cases, the exact
 msign limit of convergent coefficient sets, scalar fixed points of g,
-symmetries, the Gram rewrite and the singular-value band."""
+symmetries, the Gram rewrite and the singular-value band.  Every test runs on
+both references: the numpy one and the plain C++ one (oracle/muon_ref.cpp),
+which share no code."""
 import json
 import math
 import os
@@ -10,8 +12,16 @@ import numpy as np
 import pytest
 
 import oracle
+from oracle import cref
 
 QUINTIC = (3.4445, -4.7750, 2.0315)
+
+
+@pytest.fixture(params=["numpy", "cpp"])
+def impl(request):
+    if request.param == "numpy":
+        return oracle
+    return cref
 
 
 def rng(seed):
@@ -32,15 +42,15 @@ def rel(a, b):
 
 
 @pytest.mark.parametrize("shape", [(4, 7), (7, 4), (16, 16), (8, 24), (30, 12), (1, 5), (5, 1)])
-def test_matches_svd_closed_form(shape):
+def test_matches_svd_closed_form(shape, impl):
     G = rng(shape[0] * 100 + shape[1]).standard_normal(shape)
-    O = oracle.orthogonalize(G)
+    O = impl.orthogonalize(G)
     assert O.shape == G.shape
     assert rel(O, closed_form(G)) < 1e-12
 
 
 @pytest.mark.parametrize("method", ["standard", "gram"])
-def test_lowrank_closed_form(method):
+def test_lowrank_closed_form(method, impl):
     # a gradient of the workload kind: geometric spectrum 1..1e-3 plus noise
     r = rng(7)
     m, n, k = 24, 40, 6
@@ -50,20 +60,20 @@ def test_lowrank_closed_form(method):
     V = r.standard_normal((n, k))
     V /= np.linalg.norm(V, axis=0)
     G = (U * s) @ V.T + 1e-3 * r.standard_normal((m, n))
-    assert rel(oracle.orthogonalize(G, method=method), closed_form(G)) < 1e-10
+    assert rel(impl.orthogonalize(G, method=method), closed_form(G)) < 1e-10
 
 
-def test_diag_2x3_golden(golden_dir):
+def test_diag_2x3_golden(golden_dir, impl):
     with open(os.path.join(golden_dir, "ns_diag_2x3.json")) as f:
         gold = json.load(f)
-    O = oracle.orthogonalize(np.array(gold["G"]))
+    O = impl.orthogonalize(np.array(gold["G"]))
     assert np.allclose(O, np.array(gold["O"]), rtol=0, atol=1e-14)
     # the transposed (tall) case gives the transposed result
-    Ot = oracle.orthogonalize(np.array(gold["G"]).T)
+    Ot = impl.orthogonalize(np.array(gold["G"]).T)
     assert np.allclose(Ot, np.array(gold["O"]).T, rtol=0, atol=1e-14)
 
 
-def test_rank1(golden_dir):
+def test_rank1(golden_dir, impl):
     with open(os.path.join(golden_dir, "ns_diag_2x3.json")) as f:
         g5_1 = json.load(f)["g5_of_1"]
     r = rng(3)
@@ -72,7 +82,7 @@ def test_rank1(golden_dir):
     v = r.standard_normal(13)
     v /= np.linalg.norm(v)
     G = 2.5 * np.outer(u, v)
-    assert rel(oracle.orthogonalize(G), g5_1 * np.outer(u, v)) < 1e-13
+    assert rel(impl.orthogonalize(G), g5_1 * np.outer(u, v)) < 1e-13
 
 
 def test_scalar_map_fixed_points():
@@ -92,7 +102,7 @@ def test_scalar_map_fixed_points():
 
 
 @pytest.mark.parametrize("coeffs,steps", [((1.875, -1.25, 0.375), 40), ((1.5, -0.5, 0.0), 60)])
-def test_convergent_coeffs_reach_exact_msign(coeffs, steps):
+def test_convergent_coeffs_reach_exact_msign(coeffs, steps, impl):
     # Second-order Taylor of x^-1/2 (the page's -7/8 is read as -5/4, the only
     # value with p(1) = 1) and the Newton iteration converge to U V^T
     # ([Blog] "Orthogonalization of Gradients", theorem: O = U V^T).
@@ -103,46 +113,46 @@ def test_convergent_coeffs_reach_exact_msign(coeffs, steps):
         k = min(shape)
         S = np.linspace(1.0, 0.3, k)
         G = Q1[:, :k] @ np.diag(S) @ Q2[:, :k].T
-        O = oracle.orthogonalize(G, steps=steps, coeffs=coeffs)
+        O = impl.orthogonalize(G, steps=steps, coeffs=coeffs)
         U, _, Vt = np.linalg.svd(G, full_matrices=False)
         assert rel(O, U @ Vt) < 1e-10
         # corollary: a semi-orthogonal matrix has ||O||_F^2 = min(m, n)
         assert abs(np.sum(O * O) - min(shape)) < 1e-9
 
 
-def test_gram_equals_standard():
+def test_gram_equals_standard(impl):
     r = rng(5)
     for shape in [(12, 40), (40, 12), (16, 16), (3, 50)]:
         G = r.standard_normal(shape)
-        a = oracle.orthogonalize(G, method="standard")
-        b = oracle.orthogonalize(G, method="gram")
+        a = impl.orthogonalize(G, method="standard")
+        b = impl.orthogonalize(G, method="gram")
         assert rel(b, a) < 1e-11
 
 
-def test_per_step_schedule_matches_constant():
+def test_per_step_schedule_matches_constant(impl):
     G = rng(2).standard_normal((5, 9))
-    a = oracle.orthogonalize(G)
-    b = oracle.orthogonalize(G, coeffs=[QUINTIC] * 5)
+    a = impl.orthogonalize(G)
+    b = impl.orthogonalize(G, coeffs=[QUINTIC] * 5)
     assert np.array_equal(a, b)
     # a non-constant schedule follows the scalar composition
     sched = [QUINTIC] * 3 + [(1.5, -0.5, 0.0)] * 2
-    assert rel(oracle.orthogonalize(G, coeffs=sched), closed_form(G, 5, sched)) < 1e-12
+    assert rel(impl.orthogonalize(G, coeffs=sched), closed_form(G, 5, sched)) < 1e-12
 
 
-def test_symmetries():
+def test_symmetries(impl):
     r = rng(9)
     G = r.standard_normal((7, 11))
-    O = oracle.orthogonalize(G)
-    assert np.array_equal(oracle.orthogonalize(-G), -O)
-    assert np.array_equal(oracle.orthogonalize(G.T), O.T)
-    assert np.array_equal(oracle.orthogonalize(8.0 * G), O)
-    assert np.array_equal(oracle.orthogonalize(2.0 ** -20 * G), O)
+    O = impl.orthogonalize(G)
+    assert np.array_equal(impl.orthogonalize(-G), -O)
+    assert np.array_equal(impl.orthogonalize(G.T), O.T)
+    assert np.array_equal(impl.orthogonalize(8.0 * G), O)
+    assert np.array_equal(impl.orthogonalize(2.0 ** -20 * G), O)
     p = r.permutation(7)
     q = r.permutation(11)
-    assert rel(oracle.orthogonalize(G[p][:, q]), O[p][:, q]) < 1e-13
+    assert rel(impl.orthogonalize(G[p][:, q]), O[p][:, q]) < 1e-13
 
 
-def test_singular_value_band():
+def test_singular_value_band(impl):
     # critical points of g fix the band: g has a local max at x1 and a local
     # min at x2; once a normalized singular value has grown past ~1.6e-3, five
     # steps leave it in [g(x2), g(x1)] = [0.6818, 1.2024].  The page's
@@ -160,17 +170,17 @@ def test_singular_value_band():
     S = np.geomspace(1.0, 1e-2, m)
     assert (S / np.linalg.norm(S)).min() > 1.6e-3
     G = U @ np.diag(S) @ V[:, :m].T
-    sv = np.linalg.svd(oracle.orthogonalize(G), compute_uv=False)
+    sv = np.linalg.svd(impl.orthogonalize(G), compute_uv=False)
     assert sv.max() <= hi + 1e-12 and sv.min() >= lo - 1e-12
     # below the threshold the map is ~ a^5 x: tiny singular values stay tiny
     S2 = np.concatenate([[1.0], np.full(m - 1, 1e-6)])
     G2 = U @ np.diag(S2) @ V[:, :m].T
-    sv2 = np.sort(np.linalg.svd(oracle.orthogonalize(G2), compute_uv=False))
+    sv2 = np.sort(np.linalg.svd(impl.orthogonalize(G2), compute_uv=False))
     assert np.allclose(sv2[:-1], a ** 5 * 1e-6, rtol=1e-4)
 
 
-def test_zero_and_empty():
-    assert np.array_equal(oracle.orthogonalize(np.zeros((3, 4))), np.zeros((3, 4)))
-    assert oracle.orthogonalize(np.zeros((0, 4))).shape == (0, 4)
+def test_zero_and_empty(impl):
+    assert np.array_equal(impl.orthogonalize(np.zeros((3, 4))), np.zeros((3, 4)))
+    assert impl.orthogonalize(np.zeros((0, 4))).shape == (0, 4)
     with pytest.raises(ValueError):
-        oracle.orthogonalize(np.ones((2, 2)), method="bogus")
+        impl.orthogonalize(np.ones((2, 2)), method="bogus")

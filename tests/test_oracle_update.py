@@ -1,5 +1,6 @@
 """Pins of the oracle's momentum, weight update, AdamW fallback, planner and
-whole step against closed forms and hand-reduced 2x3 cases."""
+whole step against closed forms and hand-reduced 2x3 cases.  The elementwise
+pins run on both references (numpy and the plain C++ one)."""
 import json
 import math
 import os
@@ -8,66 +9,72 @@ import numpy as np
 import pytest
 
 import oracle
+from oracle import cref
 from workloads import configs
 
 
-def test_momentum_three_steps_closed_form():
+@pytest.fixture(params=["numpy", "cpp"])
+def impl(request):
+    return oracle if request.param == "numpy" else cref
+
+
+def test_momentum_three_steps_closed_form(impl):
     r = np.random.default_rng(0)
     G1, G2, G3 = (r.standard_normal((2, 3)) for _ in range(3))
     mu = 0.95
     M = np.zeros((2, 3))
     for G in (G1, G2):
-        M, _ = oracle.momentum_update(M, G, mu, True)
-    M3, U3 = oracle.momentum_update(M, G3, mu, True)
+        M, _ = impl.momentum_update(M, G, mu, True)
+    M3, U3 = impl.momentum_update(M, G3, mu, True)
     assert np.allclose(M3, mu * mu * G1 + mu * G2 + G3, atol=1e-15)
     assert np.allclose(U3, G3 + mu * (mu * mu * G1 + mu * G2 + G3), atol=1e-15)
-    M3p, U3p = oracle.momentum_update(M, G3, mu, False)
+    M3p, U3p = impl.momentum_update(M, G3, mu, False)
     assert np.array_equal(U3p, M3p)
 
 
-def test_momentum_hand_2x3():
+def test_momentum_hand_2x3(impl):
     M = np.array([[1.0, -2.0, 0.5], [0.0, 4.0, -1.0]])
     G = np.array([[0.5, 0.5, 0.5], [-1.0, 0.0, 2.0]])
-    Mn, U = oracle.momentum_update(M, G, 0.5, True)
+    Mn, U = impl.momentum_update(M, G, 0.5, True)
     assert np.array_equal(Mn, [[1.0, -0.5, 0.75], [-1.0, 2.0, 1.5]])
     assert np.array_equal(U, [[1.0, 0.25, 0.875], [-1.5, 1.0, 2.75]])
 
 
 @pytest.mark.parametrize("shape,val", [((256, 512), 4.5255), ((768, 768), 5.5426),
                                        ((14336, 4096), 23.9466), ((1408, 2048), 9.0510)])
-def test_scale_values(shape, val):
-    assert abs(oracle.muon_scale(*shape) - val) < 5e-5
-    assert oracle.muon_scale(768, 768, scale_dim=2304) == pytest.approx(0.2 * 48.0)
+def test_scale_values(shape, val, impl):
+    assert abs(impl.muon_scale(*shape) - val) < 5e-5
+    assert impl.muon_scale(768, 768, scale_dim=2304) == pytest.approx(0.2 * 48.0)
 
 
-def test_weight_update_hand_2x3():
+def test_weight_update_hand_2x3(impl):
     W = np.array([[1.0, 2.0, -1.0], [0.0, 0.5, 4.0]])
     O = np.array([[0.5, 0.0, -0.5], [1.0, -1.0, 0.0]])
     lr, wd, s = 0.1, 0.5, 2.0
     # W (1 - 0.05) - 0.2 O
     exp = np.array([[0.85, 1.9, -0.85], [-0.2, 0.675, 3.8]])
-    assert np.allclose(oracle.weight_update(W, O, lr, wd, s), exp, atol=1e-15)
+    assert np.allclose(impl.weight_update(W, O, lr, wd, s), exp, atol=1e-15)
 
 
-def test_adamw_step1_closed_form():
+def test_adamw_step1_closed_form(impl):
     r = np.random.default_rng(4)
     W = r.standard_normal((2, 3))
     g = r.standard_normal((2, 3))
     lr, b1, b2, eps, wd = 3e-4, 0.9, 0.95, 1e-8, 0.1
-    Wn, m, v = oracle.adamw_update(W, g, np.zeros_like(g), np.zeros_like(g), 1, lr, b1, b2, eps, wd)
+    Wn, m, v = impl.adamw_update(W, g, np.zeros_like(g), np.zeros_like(g), 1, lr, b1, b2, eps, wd)
     k = math.sqrt(1 - b2)
     assert np.allclose(Wn - W, -lr * wd * W - lr * k * g / (eps + k * np.abs(g)), rtol=1e-12, atol=1e-18)
     assert np.allclose(m, (1 - b1) * g) and np.allclose(v, (1 - b2) * g * g)
 
 
-def test_adamw_step2_hand():
+def test_adamw_step2_hand(impl):
     # scalars: g1 = 2, g2 = -1, beta1 = 0.5, beta2 = 0.75, eps = 0, lr = 1, wd = 0
     W = np.array([[0.0]])
-    W1, m, v = oracle.adamw_update(W, np.array([[2.0]]), np.zeros((1, 1)), np.zeros((1, 1)),
+    W1, m, v = impl.adamw_update(W, np.array([[2.0]]), np.zeros((1, 1)), np.zeros((1, 1)),
                                    1, 1.0, 0.5, 0.75, 0.0, 0.0)
     # m1 = 1, v1 = 1, scale = 0.5 / sqrt(0.25) = 1, W1 = -1
     assert W1[0, 0] == pytest.approx(-1.0)
-    W2, m, v = oracle.adamw_update(W1, np.array([[-1.0]]), m, v, 2, 1.0, 0.5, 0.75, 0.0, 0.0)
+    W2, m, v = impl.adamw_update(W1, np.array([[-1.0]]), m, v, 2, 1.0, 0.5, 0.75, 0.0, 0.0)
     # m2 = 0, v2 = 0.75*1 + 0.25*1 = 1 -> u = 0, W unchanged
     assert m[0, 0] == pytest.approx(0.0) and v[0, 0] == pytest.approx(1.0)
     assert W2[0, 0] == pytest.approx(-1.0)
