@@ -96,14 +96,37 @@ typedef struct {
   float* update_out;
 } muon_param_ptrs;
 
+/* Scale of the orthogonalized update O in W <- W (1 - lr wd) - lr scale O,
+ * per unit, with d_out x d_in the unit's shape in parameter layout (rows x
+ * cols) and D = scale_dim if set, else max(d_out, d_in):
+ *   MUON_SCALE_MOONLIGHT  rms_scale * sqrt(D)            ([Moonlight]
+ *                         "参数更新尺度调整": matched update RMS, 0.2)
+ *   MUON_SCALE_SPECTRAL   sqrt(d_out / d_in)             ([Blog] "Variation
+ *                         of Muon Optimizer": dualizing under the RMS->RMS
+ *                         norm, the muP form)
+ *   MUON_SCALE_UNIT_RMS   sqrt(D)                        ([Blog] DeepSeek-V4
+ *                         listing, "Rescale update RMS", with gamma below)
+ * each multiplied by extra_scale (the listing's update rescaling factor
+ * gamma; [MindSpeed] --muon-extra-scale-factor).  MindSpeed names the modes
+ * spectral / unit_rms_norm / shape_scaling without defining them; they are
+ * read as SPECTRAL / UNIT_RMS / MOONLIGHT. */
+typedef enum {
+  MUON_SCALE_MOONLIGHT = 0,
+  MUON_SCALE_SPECTRAL = 1,
+  MUON_SCALE_UNIT_RMS = 2
+} muon_scale_mode;
+
 /* Hyperparameters of one step.
  *   lr, momentum, weight_decay, nesterov, ns_steps: the Muon rule
  *     ([Blog] "Formulation of Muon Optimizer"; [Moonlight] "权重衰减机制").
  *   coeffs: host array of ns_steps*3 floats (a_k, b_k, c_k) or NULL for the
  *     quintic (3.4445, -4.7750, 2.0315) at every step ([Blog] "Newton-Schulz
  *     Iteration").
- *   rms_scale: 0.2 in [Moonlight]; the update is
- *     W <- W (1 - lr wd) - lr rms_scale sqrt(max(A,B)) O.
+ *   rms_scale: 0.2 in [Moonlight]; with the default scale mode the update
+ *     is W <- W (1 - lr wd) - lr rms_scale sqrt(max(A,B)) O.
+ *   scale_mode: muon_scale_mode (0 = MOONLIGHT).
+ *   extra_scale: multiplier of the scale; 0 is read as 1 (so a zeroed struct
+ *     keeps the default rule).  Must be finite and >= 0.
  *   adam_*: the AdamW backup of the [Moonlight] code; adam_step is t >= 1
  *     (already incremented): W <- W (1 - lr wd) - lr sqrt(1-b2^t)/(1-b1^t) *
  *     m / (eps + sqrt(v)). */
@@ -121,6 +144,8 @@ typedef struct {
   float adam_eps;
   float adam_weight_decay;
   int64_t adam_step;
+  int32_t scale_mode;
+  float extra_scale;
 } muon_hparams;
 
 /* Plan options.
@@ -198,6 +223,25 @@ typedef struct {
 
 muon_status muon_timing_enable(int32_t enable);
 muon_status muon_timing_collect(muon_kernel_timing* out, int32_t cap, int32_t* n);
+
+/* Newton-Schulz coefficient schedules: writes steps x 3 floats (a_k, b_k,
+ * c_k) to out (capacity cap floats) for muon_hparams.coeffs.
+ *   MUON_COEFF_QUINTIC  (3.4445, -4.7750, 2.0315) at every step ([Blog]
+ *                       "Newton-Schulz Iteration"; [MindSpeed]
+ *                       --muon-coefficient-type quintic).
+ *   MUON_COEFF_HYBRID   the quintic for steps-2 steps, then two refining
+ *                       steps ([Blog] DeepSeek-V4 listing: HybridNewtonSchulz,
+ *                       ten steps, eight with the quintic and two with an
+ *                       improved Newton iteration that brings the singular
+ *                       values closer to 1).  The refined coefficients are not
+ *                       printed; the reading taken is (15/8, -5/4, 3/8), the
+ *                       odd quintic with p(1) = 1, p'(1) = p''(1) = 0 (the
+ *                       second-order expansion of [Blog] "Sign of a Matrix").
+ *                       steps >= 2.
+ * Errors: MUON_E_ARG (unknown kind, steps out of [1, 64], hybrid with
+ * steps < 2, null out), MUON_E_CAPACITY (cap < 3 steps). */
+typedef enum { MUON_COEFF_QUINTIC = 0, MUON_COEFF_HYBRID = 1 } muon_coeff_kind;
+muon_status muon_ns_coefficients(int32_t kind, int32_t steps, float* out, size_t cap);
 
 /* Static text for a status code. */
 const char* muon_status_string(int32_t status);

@@ -21,11 +21,13 @@ STATUS = {0: "MUON_OK", -1: "MUON_E_ARG", -2: "MUON_E_SHAPE", -3: "MUON_E_DTYPE"
 MUON_NS_STANDARD, MUON_NS_GRAM = 0, 1
 MUON_F32, MUON_BF16 = 0, 1
 MUON_KIND_MUON, MUON_KIND_ADAMW = 0, 1
+MUON_SCALE_MOONLIGHT, MUON_SCALE_SPECTRAL, MUON_SCALE_UNIT_RMS = 0, 1, 2
+MUON_COEFF_QUINTIC, MUON_COEFF_HYBRID = 0, 1
 
 EXPORTED = ["muon_plan_create", "muon_plan_destroy", "muon_plan_workspace_bytes",
             "muon_plan_buckets", "muon_plan_units", "muon_step", "ns_orthogonalize",
             "ns_orthogonalize_workspace_bytes", "muon_timing_enable", "muon_timing_collect",
-            "muon_status_string", "muon_version"]
+            "muon_ns_coefficients", "muon_status_string", "muon_version"]
 
 
 class MuonError(RuntimeError):
@@ -51,7 +53,8 @@ class MuonHparams(ctypes.Structure):
                 ("coeffs", ctypes.POINTER(ctypes.c_float)), ("rms_scale", ctypes.c_float),
                 ("adam_lr", ctypes.c_float), ("adam_beta1", ctypes.c_float),
                 ("adam_beta2", ctypes.c_float), ("adam_eps", ctypes.c_float),
-                ("adam_weight_decay", ctypes.c_float), ("adam_step", ctypes.c_int64)]
+                ("adam_weight_decay", ctypes.c_float), ("adam_step", ctypes.c_int64),
+                ("scale_mode", ctypes.c_int32), ("extra_scale", ctypes.c_float)]
 
 
 class MuonPlanOptions(ctypes.Structure):
@@ -99,6 +102,8 @@ def lib():
     L.muon_timing_enable.restype = i32
     L.muon_timing_collect.argtypes = [ctypes.POINTER(MuonKernelTiming), i32, ctypes.POINTER(i32)]
     L.muon_timing_collect.restype = i32
+    L.muon_ns_coefficients.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_float), sz]
+    L.muon_ns_coefficients.restype = i32
     L.muon_status_string.argtypes = [i32]
     L.muon_status_string.restype = ctypes.c_char_p
     L.muon_version.argtypes = []
@@ -198,11 +203,12 @@ def muon_plan_units(plan: Plan) -> List[tuple]:
 
 def make_hparams(lr=0.02, momentum=0.95, weight_decay=0.1, nesterov=True, ns_steps=5, coeffs=None,
                  rms_scale=0.2, adam_lr=3e-4, adam_beta1=0.9, adam_beta2=0.95, adam_eps=1e-8,
-                 adam_weight_decay=0.1, adam_step=1):
+                 adam_weight_decay=0.1, adam_step=1, scale_mode=MUON_SCALE_MOONLIGHT, extra_scale=1.0):
     ca = _coeff_array(coeffs, ns_steps)
     hp = MuonHparams(lr, momentum, weight_decay, 1 if nesterov else 0, ns_steps,
                      ctypes.cast(ca, ctypes.POINTER(ctypes.c_float)) if ca is not None else None,
-                     rms_scale, adam_lr, adam_beta1, adam_beta2, adam_eps, adam_weight_decay, adam_step)
+                     rms_scale, adam_lr, adam_beta1, adam_beta2, adam_eps, adam_weight_decay, adam_step,
+                     scale_mode, extra_scale)
     hp._keep = ca  # keep the coefficient array alive with the struct
     return hp
 
@@ -274,6 +280,14 @@ def muon_timing_collect() -> dict:
 
 def muon_status_string(status: int) -> str:
     return lib().muon_status_string(status).decode()
+
+
+def muon_ns_coefficients(kind: int, steps: int):
+    """steps x 3 Newton-Schulz coefficients of a schedule kind, as a list of
+    (a, b, c) tuples."""
+    buf = (ctypes.c_float * (3 * steps))() if steps > 0 else (ctypes.c_float * 3)()
+    _check("muon_ns_coefficients", lib().muon_ns_coefficients(kind, steps, buf, 3 * max(steps, 0)))
+    return [tuple(buf[3 * k:3 * k + 3]) for k in range(steps)]
 
 
 def muon_version() -> int:

@@ -249,6 +249,17 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
 
 bool finite(float x) { return std::isfinite(x); }
 
+// Update scale of one unit (muon_scale_mode); u.rows x u.cols is the unit in
+// parameter layout, u.scale_dim the resolved D.
+double unit_scale(const muon_hparams& hp, const PlanUnit& u) {
+  const double gamma = hp.extra_scale == 0.f ? 1.0 : (double)hp.extra_scale;
+  switch (hp.scale_mode) {
+    case MUON_SCALE_SPECTRAL: return gamma * std::sqrt((double)u.rows / (double)u.cols);
+    case MUON_SCALE_UNIT_RMS: return gamma * std::sqrt((double)u.scale_dim);
+    default: return gamma * (double)hp.rms_scale * std::sqrt((double)u.scale_dim);
+  }
+}
+
 muon_status coeff_table(int32_t steps, const float* coeffs, std::vector<float>& out) {
   if (steps < 1 || steps > MAX_NS_STEPS) return MUON_E_ARG;
   out.resize((size_t)steps * 3);
@@ -272,7 +283,20 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 extern "C" {
 
-int32_t muon_version(void) { return 100; }
+int32_t muon_version(void) { return 101; }
+
+muon_status muon_ns_coefficients(int32_t kind, int32_t steps, float* out, size_t cap) {
+  if (!out || steps < 1 || steps > MAX_NS_STEPS) return MUON_E_ARG;
+  if (kind != MUON_COEFF_QUINTIC && kind != MUON_COEFF_HYBRID) return MUON_E_ARG;
+  if (kind == MUON_COEFF_HYBRID && steps < 2) return MUON_E_ARG;
+  if (cap < (size_t)steps * 3) return MUON_E_CAPACITY;
+  const float refined[3] = {1.875f, -1.25f, 0.375f};
+  for (int32_t k = 0; k < steps; ++k) {
+    const float* c = (kind == MUON_COEFF_HYBRID && k >= steps - 2) ? refined : kQuintic;
+    for (int j = 0; j < 3; ++j) out[3 * k + j] = c[j];
+  }
+  return MUON_OK;
+}
 
 const char* muon_status_string(int32_t s) {
   switch (s) {
@@ -352,6 +376,10 @@ muon_status muon_step(const muon_plan* plan, const muon_param_ptrs* ptrs, int32_
   if (st != MUON_OK) return st;
   if (!finite(hp->lr) || !finite(hp->momentum) || !finite(hp->weight_decay) || !finite(hp->rms_scale))
     return MUON_E_ARG;
+  if (!finite(hp->extra_scale) || hp->extra_scale < 0.f) return MUON_E_ARG;
+  if (hp->scale_mode != MUON_SCALE_MOONLIGHT && hp->scale_mode != MUON_SCALE_SPECTRAL &&
+      hp->scale_mode != MUON_SCALE_UNIT_RMS)
+    return MUON_E_ARG;
   if (!P.adam.empty()) {
     if (!finite(hp->adam_lr) || !finite(hp->adam_beta1) || !finite(hp->adam_beta2) ||
         !finite(hp->adam_eps) || !finite(hp->adam_weight_decay) || hp->adam_step < 1)
@@ -393,7 +421,7 @@ muon_status muon_step(const muon_plan* plan, const muon_param_ptrs* ptrs, int32_
     d.w = static_cast<char*>(q.param) + off * es;
     d.o = q.update_out ? q.update_out + off : nullptr;
     d.ld = s.cols;
-    d.scale = (float)((double)hp->rms_scale * std::sqrt((double)u.scale_dim));
+    d.scale = (float)unit_scale(*hp, u);
     hd[i] = d;
   }
   std::vector<AdamDesc> ad;

@@ -42,6 +42,11 @@ def lib():
         L.ref_orthogonalize.restype = ctypes.c_int32
         L.ref_muon_scale.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double]
         L.ref_muon_scale.restype = ctypes.c_double
+        L.ref_muon_scale_mode.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
+                                          ctypes.c_int32, ctypes.c_double]
+        L.ref_muon_scale_mode.restype = ctypes.c_double
+        L.ref_coefficients.argtypes = [ctypes.c_int32, ctypes.c_int32, _D]
+        L.ref_coefficients.restype = ctypes.c_int32
         L.ref_weight_update.argtypes = [_D, _D, ctypes.c_int64, ctypes.c_double, ctypes.c_double,
                                         ctypes.c_double]
         L.ref_adamw.argtypes = [_D, _D, _D, _D, ctypes.c_int64, ctypes.c_int64, ctypes.c_double,
@@ -101,8 +106,22 @@ def orthogonalize(G, steps: int = 5, coeffs: Optional[Sequence] = None, method: 
     return O
 
 
-def muon_scale(rows: int, cols: int, scale_dim: int = 0, rms_scale: float = 0.2) -> float:
-    return float(lib().ref_muon_scale(rows, cols, scale_dim, rms_scale))
+_MODES = {"moonlight": 0, "spectral": 1, "unit_rms": 2}
+
+
+def muon_scale(rows: int, cols: int, scale_dim: int = 0, rms_scale: float = 0.2, mode: str = "moonlight",
+               gamma: float = 1.0) -> float:
+    if mode not in _MODES:
+        raise ValueError(f"unknown scale mode {mode!r}")
+    return float(lib().ref_muon_scale_mode(rows, cols, scale_dim, rms_scale, _MODES[mode], gamma))
+
+
+def coefficients(kind: str, steps: int):
+    """steps x 3 schedule: "quintic" or "hybrid" (steps >= 2)."""
+    out = np.zeros((max(steps, 1), 3))
+    if lib().ref_coefficients({"quintic": 0, "hybrid": 1}[kind], steps, _p(out)) != 0:
+        raise ValueError("bad schedule")
+    return [tuple(r) for r in out[:steps].tolist()]
 
 
 def weight_update(W, O, lr: float, wd: float, scale: float):

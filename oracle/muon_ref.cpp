@@ -181,12 +181,40 @@ int32_t ref_orthogonalize(const double* G, int64_t rows, int64_t cols, int32_t s
   return 0;
 }
 
-// [Moonlight] "参数更新尺度调整": scale = 0.2 sqrt(max(A, B)) (rms_scale = 0.2);
-// scale_dim > 0 replaces max(A, B) (the reading for split blocks is the
-// block's own shape).
-double ref_muon_scale(int64_t rows, int64_t cols, int64_t scale_dim, double rms_scale) {
+// Scale of the orthogonalized update of a rows x cols unit (d_out x d_in),
+// D = scale_dim if > 0 else max(rows, cols) (the reading for split blocks is
+// the block's own shape):
+//   mode 0: rms_scale sqrt(D)      [Moonlight] "参数更新尺度调整" (0.2)
+//   mode 1: sqrt(d_out / d_in)     [Blog] "Variation of Muon Optimizer" (muP)
+//   mode 2: sqrt(D)                [Blog] DeepSeek-V4 listing, "Rescale update RMS"
+// times gamma (the listing's update rescaling factor).  Returns -1 for an
+// unknown mode.
+double ref_muon_scale_mode(int64_t rows, int64_t cols, int64_t scale_dim, double rms_scale, int32_t mode,
+                           double gamma) {
   const int64_t d = scale_dim > 0 ? scale_dim : std::max(rows, cols);
-  return rms_scale * std::sqrt((double)d);
+  switch (mode) {
+    case 0: return gamma * rms_scale * std::sqrt((double)d);
+    case 1: return gamma * std::sqrt((double)rows / (double)cols);
+    case 2: return gamma * std::sqrt((double)d);
+  }
+  return -1.0;
+}
+
+double ref_muon_scale(int64_t rows, int64_t cols, int64_t scale_dim, double rms_scale) {
+  return ref_muon_scale_mode(rows, cols, scale_dim, rms_scale, 0, 1.0);
+}
+
+// [Blog] DeepSeek-V4 listing: ten Newton-Schulz steps, eight with the quintic
+// and two with an improved Newton iteration (coefficients not printed; read
+// as the odd quintic with p(1) = 1, p'(1) = p''(1) = 0: (15/8, -5/4, 3/8)).
+// kind 0: quintic every step; kind 1: that hybrid, steps >= 2.  Writes
+// steps x 3 doubles; returns 0 or -1.
+int32_t ref_coefficients(int32_t kind, int32_t steps, double* out) {
+  if (steps < 1 || (kind != 0 && kind != 1) || (kind == 1 && steps < 2)) return -1;
+  const double refined[3] = {15.0 / 8.0, -5.0 / 4.0, 3.0 / 8.0};
+  for (int32_t k = 0; k < steps; ++k)
+    for (int j = 0; j < 3; ++j) out[3 * k + j] = (kind == 1 && k >= steps - 2) ? refined[j] : kQuintic[j];
+  return 0;
 }
 
 // [Moonlight] "权重衰减机制" / "代码": W <- W (1 - lr wd) - lr scale O.

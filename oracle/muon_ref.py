@@ -40,6 +40,21 @@ DEFAULT_STEPS = 5
 RMS_SCALE = 0.2
 
 
+# [Blog] DeepSeek-V4 listing: "HybridNewtonSchulz" runs ten steps, eight with
+# the quintic and the last two with an improved Newton iteration that brings
+# the singular values closer to 1.  Its coefficients are not printed; the
+# reading taken is the odd quintic p with p(1) = 1, p'(1) = p''(1) = 0, the
+# second-order expansion of x (x^2)^(-1/2) around 1 ([Blog] "Sign of a Matrix").
+REFINED = (15.0 / 8.0, -5.0 / 4.0, 3.0 / 8.0)
+
+
+def hybrid_schedule(steps: int) -> List[Tuple[float, float, float]]:
+    """steps - 2 quintic steps, then two refining steps (steps >= 2)."""
+    if steps < 2:
+        raise ValueError("the hybrid schedule needs at least two steps")
+    return [QUINTIC] * (steps - 2) + [REFINED] * 2
+
+
 def coeff_schedule(steps: int, coeffs: Optional[Sequence] = None) -> List[Tuple[float, float, float]]:
     """Per-step (a, b, c).  ``coeffs`` is None (the quintic every step), one
     triple (used every step) or a list of ``steps`` triples."""
@@ -161,14 +176,27 @@ def quintic_scalar(x: float, steps: int = DEFAULT_STEPS, coeffs=None) -> float:
 # Update  ([Moonlight] "权重衰减机制", "参数更新尺度调整", "代码")
 # --------------------------------------------------------------------------
 
-def muon_scale(rows: int, cols: int, scale_dim: int = 0, rms_scale: float = RMS_SCALE) -> float:
-    """0.2 * sqrt(max(A, B)) ([Moonlight] "参数更新尺度调整"; the code's
-    ``adjust_lr_for_muon``).  For a split block the reading taken is the
-    block's own shape ([Blog] DeepSeek-V4 listing rescales each logically
-    independent weight by sqrt(max(n, m))); ``scale_dim`` > 0 overrides
-    max(A, B)."""
+def muon_scale(rows: int, cols: int, scale_dim: int = 0, rms_scale: float = RMS_SCALE,
+               mode: str = "moonlight", gamma: float = 1.0) -> float:
+    """Scale of the orthogonalized update of a rows x cols unit (d_out x d_in).
+    "moonlight": 0.2 * sqrt(max(A, B)) ([Moonlight] "参数更新尺度调整"; the
+    code's ``adjust_lr_for_muon``); "spectral": sqrt(d_out / d_in) ([Blog]
+    "Variation of Muon Optimizer", the muP form from dualizing under the
+    RMS->RMS norm); "unit_rms": sqrt(max(n, m)) ([Blog] DeepSeek-V4 listing,
+    "Rescale update RMS").  Each is multiplied by gamma, the listing's update
+    rescaling factor.  For a split block the reading taken is the block's own
+    shape (the listing rescales each logically independent weight);
+    ``scale_dim`` > 0 overrides max(A, B)."""
     d = scale_dim if scale_dim > 0 else max(rows, cols)
-    return rms_scale * math.sqrt(d)
+    if mode == "moonlight":
+        s = rms_scale * math.sqrt(d)
+    elif mode == "spectral":
+        s = math.sqrt(rows / cols)
+    elif mode == "unit_rms":
+        s = math.sqrt(d)
+    else:
+        raise ValueError(f"unknown scale mode {mode!r}")
+    return gamma * s
 
 
 def weight_update(W: np.ndarray, O: np.ndarray, lr: float, wd: float, scale: float) -> np.ndarray:
@@ -295,6 +323,8 @@ class OracleHparams:
     adam_eps: float = 1e-8
     adam_weight_decay: float = 0.1
     adam_step: int = 1
+    scale_mode: str = "moonlight"
+    extra_scale: float = 1.0
 
 
 def muon_step(table, params, grads, moms, exp_avgs, exp_avg_sqs, hp: OracleHparams,
@@ -322,7 +352,7 @@ def muon_step(table, params, grads, moms, exp_avgs, exp_avg_sqs, hp: OracleHpara
         M_new, U = momentum_update(M, G, hp.momentum, hp.nesterov)
         M_out[u.param][r0:r1] = M_new
         O = orthogonalize(U, hp.ns_steps, hp.coeffs, method)
-        scale = muon_scale(u.rows, u.cols, u.scale_dim, hp.rms_scale)
+        scale = muon_scale(u.rows, u.cols, u.scale_dim, hp.rms_scale, hp.scale_mode, hp.extra_scale)
         W = np.asarray(params[u.param], dtype=np.float64)[r0:r1]
         W_out[u.param][r0:r1] = weight_update(W, O, hp.lr, hp.weight_decay, scale)
         if want_updates:

@@ -144,6 +144,10 @@ def test_step_validation_before_any_launch():
     assert L.muon_step(plan.handle, ptrs, 1, ctypes.byref(bad), 0x10000, ws, None) == -1
     bad = mo.make_hparams(ns_steps=2, coeffs=[(1.0, float("inf"), 0.0), (1.0, 0.0, 0.0)])
     assert L.muon_step(plan.handle, ptrs, 1, ctypes.byref(bad), 0x10000, ws, None) == -1
+    # unknown scale mode, negative or non-finite extra scale
+    for bad in (mo.make_hparams(scale_mode=3), mo.make_hparams(extra_scale=-1.0),
+                mo.make_hparams(extra_scale=float("inf"))):
+        assert L.muon_step(plan.handle, ptrs, 1, ctypes.byref(bad), 0x10000, ws, None) == -1
 
 
 def test_ns_orthogonalize_validation():

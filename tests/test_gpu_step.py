@@ -175,3 +175,47 @@ def test_mixed_precision_parameters(pdt, ns_dtype):
         tol_w = tol_o if pdt == 0 else 2e-2
         assert rel(f64(P[i]) - W0[i], w_ref - W0[i]) <= tol_w
         assert rel(f64(M[i]), ref["M"][i]) <= 1e-6
+
+
+@pytest.mark.parametrize("mode,gamma,sched", [("spectral", 1.0, "quintic"), ("unit_rms", 0.18, "hybrid"),
+                                               ("moonlight", 2.0, "hybrid")])
+def test_scale_modes_and_hybrid_schedule(mode, gamma, sched):
+    """Update-scale modes with an extra factor, and the ten-step hybrid
+    schedule (eight quintic steps, two refining ones), on a wide and a tall
+    bf16 unit."""
+    print(f"muon_step scale_mode={mode} gamma={gamma} schedule={sched}", flush=True)
+    d = dev()
+    table = [(0, 1, 512, 1536, 0, 0), (0, 1, 1536, 512, 0, 0)]
+    hpd = configs._hp(ns_steps=10 if sched == "hybrid" else 5)
+    wl = configs.Workload("modes", table, ["wide", "tall"], rank=8, hp=hpd)
+    P, M, EA, ES = _state(wl, d)
+    G = gen.make_grads(wl, 0, "cpu")
+    W0 = [f64(p) for p in P]
+    outs = [torch.zeros(r[2], r[3], dtype=torch.float32, device=d) for r in table]
+    kind = mo.MUON_COEFF_HYBRID if sched == "hybrid" else mo.MUON_COEFF_QUINTIC
+    coeffs = mo.muon_ns_coefficients(kind, hpd["ns_steps"])
+    code = {"moonlight": mo.MUON_SCALE_MOONLIGHT, "spectral": mo.MUON_SCALE_SPECTRAL,
+            "unit_rms": mo.MUON_SCALE_UNIT_RMS}[mode]
+    hp = mo.make_hparams(lr=hpd["lr"], momentum=hpd["momentum"], weight_decay=hpd["weight_decay"],
+                         nesterov=hpd["nesterov"], ns_steps=hpd["ns_steps"], coeffs=coeffs,
+                         scale_mode=code, extra_scale=gamma)
+    StepRunner(table, device=d).step(P, [g.to(d) for g in G], M, EA, ES, hp, update_outs=outs)
+    torch.cuda.synchronize()
+    ohp = _oracle_hp(hpd)
+    ohp.coeffs = oracle.hybrid_schedule(10) if sched == "hybrid" else None
+    ohp.scale_mode, ohp.extra_scale = mode, gamma
+    ref = oracle.muon_step(table, W0, [f64(g) for g in G], [np.zeros((r[2], r[3])) for r in table],
+                           [None, None], [None, None], ohp, want_updates=True)
+    for i, r in enumerate(table):
+        assert rel(f64(outs[i]), ref["O"][i]) <= 2e-2, (i, rel(f64(outs[i]), ref["O"][i]))
+        # the stored weight is W (1 - lr wd) - lr scale O with the GPU's own O
+        # and the oracle's scale, rounded to bf16: equal up to one bf16 ulp
+        # (the fp32 rounding decision).  A comparison of dW with the oracle's
+        # is not meaningful here: at spectral scale the step is a few ulps of W.
+        scale = oracle.muon_scale(r[2], r[3], 0, 0.2, mode, gamma)
+        w_exp = W0[i] * (1.0 - hpd["lr"] * hpd["weight_decay"]) - hpd["lr"] * scale * f64(outs[i])
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(w_exp), 1e-30))) - 7)
+        # plus the fp32 evaluation error, which matters where the two terms cancel
+        f32err = 4 * 2.0 ** -24 * (np.abs(W0[i]) + hpd["lr"] * scale * np.abs(f64(outs[i])))
+        err = np.abs(f64(P[i]) - stored(w_exp, torch.bfloat16))
+        assert np.all(err <= 1.01 * ulp + f32err), float(np.max(err - 1.01 * ulp - f32err))
