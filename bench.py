@@ -37,6 +37,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default="llama3_8b_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--ns-method", choices=["standard", "gram", "auto"], default=None,
+                   help="override the workload's Newton-Schulz method")
     p.add_argument("--cpu-sample", default=",".join(["1024x4096"] * 8),
                    help="unit shapes the oracle is timed on")
     return p.parse_args()
@@ -56,7 +58,9 @@ def main():
     mo.lib()
     dev = torch.device("cuda:0")
     wl = configs.ALL[args.workload]()
-    method = 1 if wl.method == "gram" else 0
+    if args.ns_method:
+        wl.method = args.ns_method
+    method = {"standard": 0, "gram": 1, "auto": 2}[wl.method]
     table = wl.table
 
     # ---- inputs (untimed), resident in HBM
@@ -123,7 +127,7 @@ def main():
                 "flops_per_launch": d["flops"] / d["launches"],
                 "avg_launch_ms": d["total_ms"] / d["launches"], "traffic": None}
     if dom == "ns_update_aX_BX" and wl.method == "standard":
-        # algorithmic HBM bytes of the update GEMM: read Y and B, write Y' and X'
+        # algorithmic HBM bytes of the update GEMM: read Y and P, write Y' and X'
         es = 2 if table[0][1] == 1 else 4
         per_step = sum(es * (3.0 * m * n + 1.0 * m * m) for m, n in unit_shapes(table))
         roofline["algorithmic_bytes_per_launch"] = (wl.hp["ns_steps"] - 1) * per_step * args.steps / d["launches"]
@@ -172,8 +176,10 @@ def unit_shapes(table):
     return out
 
 
+# the update GEMM's traffic depends on the kernel and on the launch arguments
 GEMM_SOURCES = ("matrix_orthogonalizing_optimizer_amd/csrc/gemm.hpp",
-                "matrix_orthogonalizing_optimizer_amd/csrc/gemm_bf16.hip")
+                "matrix_orthogonalizing_optimizer_amd/csrc/gemm_bf16.hip",
+                "matrix_orthogonalizing_optimizer_amd/csrc/api.cpp")
 
 
 def gemm_source_digest() -> str:

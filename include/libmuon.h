@@ -50,8 +50,13 @@ typedef enum {
   MUON_E_CAPACITY = -8   /* output array too small (query calls) */
 } muon_status;
 
-/* [DeepSpeed] NS_METHODS = {standard, gram}. */
-typedef enum { MUON_NS_STANDARD = 0, MUON_NS_GRAM = 1 } muon_ns_method;
+/* [DeepSpeed] NS_METHODS = {standard, gram}.  MUON_NS_AUTO picks per unit
+ * (m = min, n = max of its sides): Gram where it does less work, n/m > 5/3
+ * (executed cost with symmetric products: standard steps (3 m^2 n + m^3),
+ * Gram 3 m^2 n + (6 steps - 5) m^3), and only for m >= 512, where its
+ * power-of-two scaled fp16 chain stays within the bf16 tolerance; standard
+ * otherwise.  Plans report the method each bucket resolved to. */
+typedef enum { MUON_NS_STANDARD = 0, MUON_NS_GRAM = 1, MUON_NS_AUTO = 2 } muon_ns_method;
 
 /* Storage dtype of parameters and gradients.  Momentum and AdamW moments are
  * always fp32. */

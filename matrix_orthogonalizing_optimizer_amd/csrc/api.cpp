@@ -9,9 +9,10 @@
 //   norm   s^2 per unit, 1/s, 1/s^2                      [norm_finalize_kernel]
 //   k = 0..steps-1 with (a_k, b_k, c_k):
 //     A = X X^T            (k = 0: times 1/s^2, folding X0 = U / s)
-//     B = c A A + b A      (symmetric: upper tiles, mirror-written)
-//     X' = a X + B X       (k = 0: times 1/s); the last step's epilogue
-//                          applies W <- W (1 - lr wd) - lr scale O directly
+//     P = a I + b A + c A A (symmetric: upper tiles, mirror-written)
+//     X' = P X = a X + (b A + c A^2) X   (k = 0: times 1/s), computed as
+//                          Y' = Y P^T on the transposed copy; the last step's
+//                          epilogue applies W <- W (1 - lr wd) - lr scale O
 // Gram method (DeepSpeed page: iterate on the square Gram matrix R = X X^T):
 //   R = 2^e X0 X0^T / s^2 (power-of-two scaled, fp16 for a bf16 bucket);
 //   P_k = a I + b R + c R^2;  Q <- P_k Q;  R <- P_k R P_k;  O = Q X0 / s.
@@ -147,17 +148,17 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
       g.alphaSel = k == 0 ? SEL_INV_S2 : SEL_ONE;
       g.aux = d_aux;
       HIP_TRY(timed(F_SYRK, mm_n, 0.0, st, [&] { return launch_gemm(T, cdt, cdt, true, EPI_SCALE, g, st); }));
-      // B = c A A^T + b A
+      // P = a I + b A + c A A^T  (a X + (b A + c A^2) X = P X: the a X term
+      // rides on P's diagonal, so the update reads no addend)
       g = sym_args(A, b.mp, ss, A, b.mp, ss, (int)m, B);
       g.E = A; g.lde = b.mp; g.sE = ss;
-      g.alpha = cc; g.beta = cb; g.gamma = 0.f;
+      g.alpha = cc; g.beta = cb; g.gamma = ca;
       HIP_TRY(timed(F_POLY, mmm, 0.0, st, [&] { return launch_gemm(T, cdt, cdt, true, EPI_POLY, g, st); }));
-      // Y' = a Y + Y B^T  (k = 0: (a U + B U)^T / s); stores Y' and X' = Y'^T
+      // Y' = Y P^T  (k = 0: (P U)^T / s); stores Y' and X' = Y'^T
       g = gemm_args(T, cnt, (int)n, (int)m, (int)m, false);
       g.L = Y[k & 1]; g.ldl = b.mp; g.sL = sy;
       g.R = B; g.ldr = b.mp; g.sR = ss;
-      g.E = Y[k & 1]; g.lde = b.mp; g.sE = sy;
-      g.alpha = 1.f; g.beta = ca;
+      g.alpha = 1.f; g.beta = 0.f;
       g.alphaSel = k == 0 ? SEL_INV_S : SEL_ONE;
       g.aux = d_aux;
       if (k + 1 < cp.steps) {
@@ -510,7 +511,7 @@ static void ns_layout(const PlanBucket& b, size_t& off_aux, size_t& off_part, si
 
 static muon_status ns_bucket(int64_t rows, int64_t cols, int32_t dtype, int32_t method, PlanBucket& b) {
   if (dtype != MUON_F32 && dtype != MUON_BF16) return MUON_E_DTYPE;
-  if (method != MUON_NS_STANDARD && method != MUON_NS_GRAM) return MUON_E_METHOD;
+  if (method != MUON_NS_STANDARD && method != MUON_NS_GRAM && method != MUON_NS_AUTO) return MUON_E_METHOD;
   if (rows < 0 || cols < 0 || rows > ((int64_t)1 << 30) || cols > ((int64_t)1 << 30)) return MUON_E_SHAPE;
   std::memset(&b, 0, sizeof(b));
   b.m = (int32_t)std::min(rows, cols);
@@ -518,7 +519,7 @@ static muon_status ns_bucket(int64_t rows, int64_t cols, int32_t dtype, int32_t 
   b.tall = rows > cols ? 1 : 0;
   b.pdtype = dtype;
   b.cdtype = dtype;
-  b.method = method;
+  b.method = resolve_method(method, b.m, b.n);
   b.first = 0;
   b.count = 1;
   bucket_derive(b, ~size_t(0));

@@ -21,6 +21,11 @@ int32_t elem_size(int32_t cdtype) { return cdtype == MUON_F32 ? 4 : 2; }
 
 static size_t align_ws(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALIGN; }
 
+int32_t resolve_method(int32_t method, int64_t m, int64_t n) {
+  if (method != MUON_NS_AUTO) return method;
+  return (3 * n > 5 * m && m >= 512) ? MUON_NS_GRAM : MUON_NS_STANDARD;
+}
+
 bool bucket_addressable(const PlanBucket& b) {
   // every GEMM operand of one unit is addressed with 32-bit byte offsets
   const uint64_t es = (uint64_t)elem_size(b.cdtype);
@@ -74,7 +79,8 @@ muon_status build_plan(const muon_param_shape* table, int32_t n, const muon_plan
   if (n < 0 || (n > 0 && !table)) return MUON_E_ARG;
   muon_plan_options o{MUON_NS_STANDARD, -1};
   if (opts) o = *opts;
-  if (o.ns_method != MUON_NS_STANDARD && o.ns_method != MUON_NS_GRAM) return MUON_E_METHOD;
+  if (o.ns_method != MUON_NS_STANDARD && o.ns_method != MUON_NS_GRAM && o.ns_method != MUON_NS_AUTO)
+    return MUON_E_METHOD;
   if (o.ns_dtype != -1 && o.ns_dtype != MUON_F32 && o.ns_dtype != MUON_BF16) return MUON_E_DTYPE;
   P.table.assign(table, table + n);
   P.opts = o;
@@ -114,10 +120,12 @@ muon_status build_plan(const muon_param_shape* table, int32_t n, const muon_plan
     const int32_t m = (int32_t)std::min(u.rows, u.cols), nn = (int32_t)std::max(u.rows, u.cols);
     const int32_t pdt = P.table[u.param].dtype;
     const int32_t cdt = o.ns_dtype < 0 ? pdt : o.ns_dtype;
+    const int32_t meth = resolve_method(o.ns_method, m, nn);
     size_t bi = 0;
     for (; bi < P.buckets.size(); ++bi) {
       const PlanBucket& b = P.buckets[bi];
-      if (b.m == m && b.n == nn && b.tall == u.tall && b.pdtype == pdt && b.cdtype == cdt) break;
+      if (b.m == m && b.n == nn && b.tall == u.tall && b.pdtype == pdt && b.cdtype == cdt && b.method == meth)
+        break;
     }
     if (bi == P.buckets.size()) {
       PlanBucket b{};
@@ -126,7 +134,7 @@ muon_status build_plan(const muon_param_shape* table, int32_t n, const muon_plan
       b.tall = u.tall;
       b.pdtype = pdt;
       b.cdtype = cdt;
-      b.method = o.ns_method;
+      b.method = meth;
       P.buckets.push_back(b);
       members.emplace_back();
     }

@@ -53,6 +53,7 @@ int64_t round_up(int64_t x, int64_t m);
 int32_t elem_size(int32_t cdtype);
 void bucket_derive(PlanBucket& b, size_t chunk_cap_bytes);
 bool bucket_addressable(const PlanBucket& b);  // one unit's m x n operand < 2^31 bytes
+int32_t resolve_method(int32_t method, int64_t m, int64_t n);  // MUON_NS_AUTO -> standard or Gram
 size_t per_unit_data_bytes(const PlanBucket& b);
 
 muon_status build_plan(const muon_param_shape* table, int32_t n, const muon_plan_options* opts,

@@ -261,8 +261,10 @@ int64_t ref_plan(const int64_t* table, int32_t n, int32_t method, int32_t ns_dty
   for (size_t i = 0; i < order.size(); ++i) {
     const U& u = order[i];
     const int64_t pdt = table[6 * u.p + 1];
-    const std::vector<int64_t> key = {std::min(u.rows, u.cols), std::max(u.rows, u.cols), u.tall, pdt,
-                                      ns_dtype < 0 ? pdt : ns_dtype, method};
+    const int64_t m = std::min(u.rows, u.cols), nn = std::max(u.rows, u.cols);
+    // method 2: Gram where it executes less work (n/m > 5/3) and m >= 512
+    const int64_t meth = method == 2 ? ((3 * nn > 5 * m && m >= 512) ? 1 : 0) : method;
+    const std::vector<int64_t> key = {m, nn, u.tall, pdt, ns_dtype < 0 ? pdt : ns_dtype, meth};
     size_t b = 0;
     while (b < keys.size() && keys[b] != key) ++b;
     if (b == keys.size()) {

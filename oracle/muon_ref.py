@@ -278,6 +278,18 @@ def plan_units(table) -> List[OracleUnit]:
     return units
 
 
+def resolve_method(method: int, m: int, n: int) -> int:
+    """Method 2 ("auto") picks, per unit, the Gram variant where it executes
+    less work -- standard: steps (3 m^2 n + m^3) with symmetric products,
+    Gram: 3 m^2 n + (6 steps - 5) m^3, so n/m > 5/3 -- and only for m >= 512,
+    where its fp16 chain stays inside the bf16 tolerance (measured); the
+    standard method otherwise.  The pages give no rule; this is the reading
+    taken."""
+    if method != 2:
+        return method
+    return 1 if (3 * n > 5 * m and m >= 512) else 0
+
+
 def plan_buckets(table, method: int, ns_dtype: int = -1):
     """Group units with the same (m, n, tall, parameter dtype, compute dtype,
     method).  Buckets are numbered by first appearance; units inside a bucket
@@ -290,7 +302,7 @@ def plan_buckets(table, method: int, ns_dtype: int = -1):
     for ui, u in enumerate(units):
         pdt = table[u.param][1]
         dt = pdt if ns_dtype < 0 else ns_dtype
-        key = (u.m, u.n, 1 if u.tall else 0, pdt, dt, method)
+        key = (u.m, u.n, 1 if u.tall else 0, pdt, dt, resolve_method(method, u.m, u.n))
         found = -1
         for bi, k in enumerate(keys):
             if k == key:

@@ -52,10 +52,11 @@ def test_exports_every_declared_function():
 
 @pytest.mark.parametrize("name", list(configs.ALL))
 @pytest.mark.parametrize("ns_dtype", [-1, 0])
-def test_plan_matches_oracle_bit_exact(name, ns_dtype):
+@pytest.mark.parametrize("auto", [False, True])
+def test_plan_matches_oracle_bit_exact(name, ns_dtype, auto):
     _lib_or_skip()
     wl = configs.ALL[name]()
-    method = 1 if wl.method == "gram" else 0
+    method = 2 if auto else (1 if wl.method == "gram" else 0)
     plan = mo.muon_plan_create(wl.table, method, ns_dtype)
     units, keys, members = oracle.plan_buckets(wl.table, method, ns_dtype)
     got_b = mo.muon_plan_buckets(plan)
@@ -112,6 +113,16 @@ def test_plan_rejects(row, status):
     with pytest.raises(mo.MuonError) as e:
         mo.muon_plan_create([(0, 1, 4, 4, 0, 0)], ns_method=7)
     assert e.value.status == -4
+
+
+def test_auto_method_resolution():
+    _lib_or_skip()
+    # Gram only where n/m > 5/3 and m >= 512; the plan reports the resolved method
+    table = [(0, 1, 4096, 14336, 0, 0), (0, 1, 14336, 4096, 0, 0), (0, 1, 4096, 4096, 0, 0),
+             (0, 1, 1024, 4096, 0, 0), (0, 1, 256, 4096, 0, 0), (0, 1, 600, 1000, 0, 0),
+             (0, 1, 600, 1001, 0, 0)]
+    got = [b[5] for b in mo.muon_plan_buckets(mo.muon_plan_create(table, mo.MUON_NS_AUTO))]
+    assert got == [1, 1, 0, 1, 0, 0, 1]
 
 
 def test_step_validation_before_any_launch():

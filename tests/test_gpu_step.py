@@ -219,3 +219,27 @@ def test_scale_modes_and_hybrid_schedule(mode, gamma, sched):
         f32err = 4 * 2.0 ** -24 * (np.abs(W0[i]) + hpd["lr"] * scale * np.abs(f64(outs[i])))
         err = np.abs(f64(P[i]) - stored(w_exp, torch.bfloat16))
         assert np.all(err <= 1.01 * ulp + f32err), float(np.max(err - 1.01 * ulp - f32err))
+
+
+def test_auto_method_mixed_plan():
+    """One plan with ns_method auto: the wide and tall units resolve to the
+    Gram variant (n/m = 2, m = 512), the square one to the standard method;
+    every unit against the oracle."""
+    print("muon_step ns_method=auto", flush=True)
+    d = dev()
+    table = [(0, 1, 512, 1024, 0, 0), (0, 1, 512, 512, 0, 0), (0, 1, 1024, 512, 0, 0)]
+    wl = configs.Workload("auto", table, ["wide", "square", "tall"], rank=8, hp=configs._hp())
+    P, M, EA, ES = _state(wl, d)
+    G = gen.make_grads(wl, 0, "cpu")
+    W0 = [f64(p) for p in P]
+    outs = [torch.zeros(r[2], r[3], dtype=torch.float32, device=d) for r in table]
+    run = StepRunner(table, method=mo.MUON_NS_AUTO, device=d)
+    assert [b[5] for b in mo.muon_plan_buckets(run.plan)] == [1, 0, 1]
+    run.step(P, [g.to(d) for g in G], M, EA, ES, hp_from(wl.hp), update_outs=outs)
+    torch.cuda.synchronize()
+    ref = oracle.muon_step(table, W0, [f64(g) for g in G], [np.zeros((r[2], r[3])) for r in table],
+                           [None] * 3, [None] * 3, _oracle_hp(wl.hp), want_updates=True)
+    for i in range(3):
+        assert rel(f64(outs[i]), ref["O"][i]) <= 2e-2, (i, rel(f64(outs[i]), ref["O"][i]))
+        dw_ref = stored(ref["W"][i], torch.bfloat16) - W0[i]
+        assert rel(f64(P[i]) - W0[i], dw_ref) <= 2e-2
