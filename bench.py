@@ -11,7 +11,7 @@ generated on the GPU from seeded torch generators.
 
 Prints one JSON line: value = nominal Newton-Schulz TFLOP/s of the whole step
 (5 x sum over units of 4 m^2 n + 2 m^3, m <= n, divided by the step time),
-ms_per_step, the roofline of the dominant kernel (the B X update GEMM,
+ms_per_step, the roofline of the dominant kernel (the P X update GEMM,
 timed live with HIP events around each of its launches) and the fp64 oracle
 timed on the host cores on a bounded sample.
 """

@@ -210,7 +210,7 @@ muon_status ns_orthogonalize_workspace_bytes(int64_t rows, int64_t cols, int32_t
  * every kernel launch of the library is bracketed by two HIP events recorded
  * on the launch's stream, tagged with the kernel family and the algorithmic
  * FLOPs / HBM bytes of that launch:
- *   flops  Newton-Schulz contractions: 2*m*m*n (X X^T and B X) or 2*m^3
+ *   flops  Newton-Schulz contractions: 2*m*m*n (X X^T and P X) or 2*m^3
  *          (A A and the Gram m x m products) per unit, counted as dense
  *          products even where symmetry halves the executed work;
  *   bytes  elementwise kernels: bytes each element must move (momentum:

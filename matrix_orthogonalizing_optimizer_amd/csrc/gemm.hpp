@@ -5,11 +5,11 @@
 // with L_u (M x K) and R_u (N x K) both row-major with K contiguous.  The
 // Newton-Schulz step of "Muon Optimizer and the Distributed Implementation"
 // (section "Newton-Schulz Iteration"),
-//     A = X X^T,   B = b A + c A A,   X' = a X + B X,
+//     A = X X^T,   B = b A + c A A,   X' = a X + B X = P X  (P = a I + B),
 // is run with every unit kept in both orientations, X (m x n) and Y = X^T
 // (n x m): A = X X^T and B = c A A^T + b A are symmetric products (only
 // upper-triangle tiles are computed, then mirrored), and the update is
-// computed transposed, Y' = a Y + Y B^T (B is symmetric), its epilogue
+// computed transposed, Y' = Y P^T (P is symmetric), its epilogue
 // storing Y' directly and X' = Y'^T through the mirror pass.  So both
 // operands of every product are K-contiguous.
 //

@@ -10,9 +10,9 @@ enum Family : int {
   F_MOMENTUM = 0,
   F_NORM,
   F_SYRK,      // A = X X^T (standard)
-  F_POLY,      // B = b A + c A A
-  F_UPDATE,    // X' = a X + B X
-  F_FINAL,     // last X' = a X + B X fused with the parameter update
+  F_POLY,      // P = a I + b A + c A A
+  F_UPDATE,    // X' = P X (= a X + B X)
+  F_FINAL,     // last X' = P X fused with the parameter update
   F_GRAM_R0,   // R = X0 X0^T (Gram)
   F_GRAM_P,    // P = a I + b R + c R R
   F_GRAM_Q,    // Q <- P Q
