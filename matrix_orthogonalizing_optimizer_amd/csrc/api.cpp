@@ -4,7 +4,8 @@
 // Per bucket chunk (units of one shape), standard method ("Muon Optimizer and
 // the Distributed Implementation", sections "Formulation of Muon Optimizer"
 // and "Newton-Schulz Iteration"):
-//   K-M    M <- mu M + G;  U = G + mu M (Nesterov) or M;  X0 = U (wide layout)
+//   K-M    M <- mu M + G;  U = G + mu M (Nesterov) or M;  Y0 = U^T of the wide
+//          orientation (a tall parameter block already has that layout)
 //          and partial sums of U^2                      [momentum_kernel]
 //   norm   s^2 per unit, 1/s, 1/s^2                      [norm_finalize_kernel]
 //   k = 0..steps-1 with (a_k, b_k, c_k):
@@ -74,29 +75,29 @@ GemmArgs gemm_args(int tile, int32_t cnt, int M, int N, int K, bool sym) {
   } while (0)
 
 // Momentum + norm for one chunk, then the Newton-Schulz chain and the fused
-// update (or a plain store of O for ns_orthogonalize).  Every unit is kept in
-// both orientations: X (m x n, wide) and Y = X^T (n x m).
+// update (or a plain store of O for ns_orthogonalize).  Every unit is kept
+// as Y = X^T (n x m, the wide orientation transposed): the symmetric product
+// A = X X^T = Y^T Y reads Y K-major, the update Y' = Y P^T reads it row-major,
+// so one copy serves both.
 muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux, float* d_part,
                       char* data, int32_t cnt, const ChainParams& cp, hipStream_t st) {
   const int cdt = dt_dev(b.cdtype);
   const int pdt = dt_dev(b.pdtype);
   const int es = elem_size(b.cdtype);
   const int64_t m = b.m, n = b.n;
-  const int64_t sx = m * b.ldx, sy = n * b.mp, ss = m * b.mp;
-  char* X = data + b.off[0];
-  char* Y0 = data + b.off[1];
+  const int64_t sy = n * b.mp, ss = m * b.mp;
+  char* Y0 = data + b.off[0];
 
-  // K-M: the parameter block is X (wide unit) or Y (tall unit); the kernel
-  // writes it as is and transposed
+  // K-M: a tall unit's parameter block has the layout of Y (written as is), a
+  // wide unit's is X (written transposed)
   MomArgs ma;
   std::memset(&ma, 0, sizeof(ma));
   ma.desc = d_desc;
-  ma.D = b.tall ? Y0 : X;
-  ma.ldd = b.tall ? b.mp : b.ldx;
-  ma.sD = b.tall ? sy : sx;
-  ma.T = b.tall ? X : Y0;
-  ma.ldt = b.tall ? b.ldx : b.mp;
-  ma.sT = b.tall ? sx : sy;
+  if (b.tall) {
+    ma.D = Y0; ma.ldd = b.mp; ma.sD = sy;
+  } else {
+    ma.T = Y0; ma.ldt = b.mp; ma.sT = sy;
+  }
   ma.partials = d_part;
   ma.rows = (int32_t)(b.tall ? n : m);
   ma.cols = (int32_t)(b.tall ? m : n);
@@ -111,7 +112,7 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
   const double mm_n = units * 2.0 * (double)m * (double)m * (double)n;  // 2 m^2 n per unit
   const double mmm = units * 2.0 * (double)m * (double)m * (double)m;   // 2 m^3 per unit
   const double pes = b.pdtype == MUON_F32 ? 4.0 : 2.0;
-  const double km_bytes = elems * (pes + (cp.has_mom ? 8.0 : 0.0) + 2.0 * (double)es);
+  const double km_bytes = elems * (pes + (cp.has_mom ? 8.0 : 0.0) + (double)es);
   HIP_TRY(timed(F_MOMENTUM, 0.0, km_bytes, st, [&] {
     return launch_momentum(pdt, cdt, b.tall != 0, ma, (int64_t)cnt * b.km_tiles, st);
   }));
@@ -138,23 +139,25 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
   };
 
   if (b.method == MUON_NS_STANDARD) {
-    char* Y[2] = {Y0, data + b.off[2]};
-    char* A = data + b.off[3];
-    char* B = data + b.off[4];
+    char* Y[2] = {Y0, data + b.off[1]};
+    char* A = data + b.off[2];
+    char* B = data + b.off[3];
     for (int k = 0; k < cp.steps; ++k) {
       const float ca = cp.coeffs[3 * k], cb = cp.coeffs[3 * k + 1], cc = cp.coeffs[3 * k + 2];
-      // A = X X^T  (k = 0: U U^T / s^2)
-      GemmArgs g = sym_args(X, b.ldx, sx, X, b.ldx, sx, (int)n, A);
+      // A = X X^T = Y^T Y  (k = 0: U U^T / s^2), Y read K-major
+      GemmArgs g = sym_args(Y[k & 1], b.mp, sy, Y[k & 1], b.mp, sy, (int)n, A);
       g.alphaSel = k == 0 ? SEL_INV_S2 : SEL_ONE;
       g.aux = d_aux;
-      HIP_TRY(timed(F_SYRK, mm_n, 0.0, st, [&] { return launch_gemm(T, cdt, cdt, true, EPI_SCALE, g, st); }));
+      HIP_TRY(timed(F_SYRK, mm_n, 0.0, st,
+                    [&] { return launch_gemm(T, cdt, cdt, true, EPI_SCALE, true, g, st); }));
       // P = a I + b A + c A A^T  (a X + (b A + c A^2) X = P X: the a X term
       // rides on P's diagonal, so the update reads no addend)
       g = sym_args(A, b.mp, ss, A, b.mp, ss, (int)m, B);
       g.E = A; g.lde = b.mp; g.sE = ss;
       g.alpha = cc; g.beta = cb; g.gamma = ca;
-      HIP_TRY(timed(F_POLY, mmm, 0.0, st, [&] { return launch_gemm(T, cdt, cdt, true, EPI_POLY, g, st); }));
-      // Y' = Y P^T  (k = 0: (P U)^T / s); stores Y' and X' = Y'^T
+      HIP_TRY(timed(F_POLY, mmm, 0.0, st,
+                    [&] { return launch_gemm(T, cdt, cdt, true, EPI_POLY, false, g, st); }));
+      // Y' = Y P^T  (k = 0: (P U)^T / s)
       g = gemm_args(T, cnt, (int)n, (int)m, (int)m, false);
       g.L = Y[k & 1]; g.ldl = b.mp; g.sL = sy;
       g.R = B; g.ldr = b.mp; g.sR = ss;
@@ -163,12 +166,12 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
       g.aux = d_aux;
       if (k + 1 < cp.steps) {
         g.C = Y[(k + 1) & 1]; g.ldc = b.mp; g.sC = sy;
-        g.C2 = X; g.ldc2 = b.ldx; g.sC2 = sx;
-        HIP_TRY(timed(F_UPDATE, mm_n, 0.0, st, [&] { return launch_gemm(T, cdt, cdt, false, EPI_AXPY, g, st); }));
+        HIP_TRY(timed(F_UPDATE, mm_n, 0.0, st,
+                      [&] { return launch_gemm(T, cdt, cdt, false, EPI_AXPY, false, g, st); }));
       } else {
         final_args(g);
         HIP_TRY(timed(F_FINAL, mm_n, elems * 2.0 * pes, st,
-                      [&] { return launch_gemm(T, cdt, pdt, false, EPI_FINAL, g, st); }));
+                      [&] { return launch_gemm(T, cdt, pdt, false, EPI_FINAL, false, g, st); }));
       }
     }
     return MUON_OK;
@@ -184,12 +187,13 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
     while ((int64_t(1) << e) < m && e < 15) ++e;
     rs = std::ldexp(1.f, e);
   }
-  char* R = data + b.off[2];
-  char* Tm = data + b.off[3];
-  char* PZ[3] = {data + b.off[4], data + b.off[5], data + b.off[6]};
-  GemmArgs g = sym_args(X, b.ldx, sx, X, b.ldx, sx, (int)n, R);
+  char* R = data + b.off[1];
+  char* Tm = data + b.off[2];
+  char* PZ[3] = {data + b.off[3], data + b.off[4], data + b.off[5]};
+  GemmArgs g = sym_args(Y0, b.mp, sy, Y0, b.mp, sy, (int)n, R);
   g.alpha = rs; g.alphaSel = SEL_INV_S2; g.aux = d_aux;
-  HIP_TRY(timed(F_GRAM_R0, mm_n, 0.0, st, [&] { return launch_gemm(T, cdt, sdt, true, EPI_SCALE, g, st); }));
+  HIP_TRY(timed(F_GRAM_R0, mm_n, 0.0, st,
+                [&] { return launch_gemm(T, cdt, sdt, true, EPI_SCALE, true, g, st); }));
   int z = -1;  // buffer holding Z (after the last step: Q)
   for (int k = 0; k < cp.steps; ++k) {
     const bool last = k + 1 == cp.steps;
@@ -201,7 +205,7 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
     g.E = R; g.lde = b.mp; g.sE = ss;
     g.alpha = cc / (rs * rs); g.beta = cb / rs; g.gamma = ca;
     HIP_TRY(timed(F_GRAM_P, mmm, 0.0, st, [&] {
-      return launch_gemm(T, sdt, (last && k == 0) ? qdt_last : sdt, true, EPI_POLY, g, st);
+      return launch_gemm(T, sdt, (last && k == 0) ? qdt_last : sdt, true, EPI_POLY, false, g, st);
     }));
     if (k == 0) {
       z = p;  // Z_0 = P_0^T = P_0
@@ -219,7 +223,7 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
         g.C = PZ[zn]; g.ldc = b.mp; g.sC = ss;
       }
       HIP_TRY(timed(F_GRAM_Q, mmm, 0.0, st,
-                    [&] { return launch_gemm(T, sdt, last ? qdt_last : sdt, false, EPI_AXPY, g, st); }));
+                    [&] { return launch_gemm(T, sdt, last ? qdt_last : sdt, false, EPI_AXPY, false, g, st); }));
       z = zn;
     }
     if (!last) {
@@ -229,10 +233,12 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
       g.R = R; g.ldr = b.mp; g.sR = ss;
       g.C = Tm; g.ldc = b.mp; g.sC = ss;
       g.beta = 0.f;
-      HIP_TRY(timed(F_GRAM_T, mmm, 0.0, st, [&] { return launch_gemm(T, sdt, sdt, false, EPI_AXPY, g, st); }));
+      HIP_TRY(timed(F_GRAM_T, mmm, 0.0, st,
+                    [&] { return launch_gemm(T, sdt, sdt, false, EPI_AXPY, false, g, st); }));
       // R = Tm P  (P symmetric; the result is symmetric: upper tiles + mirror)
       g = sym_args(Tm, b.mp, ss, PZ[p], b.mp, ss, (int)m, R);
-      HIP_TRY(timed(F_GRAM_R, mmm, 0.0, st, [&] { return launch_gemm(T, sdt, sdt, true, EPI_SCALE, g, st); }));
+      HIP_TRY(timed(F_GRAM_R, mmm, 0.0, st,
+                    [&] { return launch_gemm(T, sdt, sdt, true, EPI_SCALE, false, g, st); }));
     }
   }
   // O^T = Y0 Q^T / s  (= (Q X0)^T / s), fused with the update
@@ -244,7 +250,7 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
   g.aux = d_aux;
   final_args(g);
   HIP_TRY(timed(F_FINAL, mm_n, elems * 2.0 * pes, st,
-                [&] { return launch_gemm(T, cdt, pdt, false, EPI_FINAL, g, st); }));
+                [&] { return launch_gemm(T, cdt, pdt, false, EPI_FINAL, false, g, st); }));
   return MUON_OK;
 }
 

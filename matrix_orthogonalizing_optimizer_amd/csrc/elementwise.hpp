@@ -13,8 +13,8 @@ namespace muon {
 // [Blog] "Formulation of Muon Optimizer": M_t = mu M_{t-1} + G_t;
 // "Variation of Muon Optimizer": Nesterov orthogonalizes mu M_t + G_t.
 // One workgroup handles a 64 x 64 tile of one unit (parameter layout) and
-// writes U in both working layouts: as is (D, leading dimension ldd) and
-// transposed through LDS (T, leading dimension ldt), pad columns zero.  A
+// writes U as is (D, leading dimension ldd) and/or transposed through LDS
+// (T, leading dimension ldt), whichever is set, pad columns zero.  A
 // 64-element row of 16-bit values is one 128-byte line, so every load and
 // store of the tile moves whole lines.  Each workgroup writes one partial sum
 // of U^2 (fp32, fixed order).
@@ -60,8 +60,8 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MomArgs a) {
   const UnitDesc d = a.desc[unit];
   const TG* __restrict__ G = reinterpret_cast<const TG*>(d.g);
   float* __restrict__ M = d.mom;
-  TX* __restrict__ X = reinterpret_cast<TX*>(a.D) + (int64_t)unit * a.sD;
-  TX* __restrict__ XT = reinterpret_cast<TX*>(a.T) + (int64_t)unit * a.sT;
+  TX* __restrict__ X = a.D ? reinterpret_cast<TX*>(a.D) + (int64_t)unit * a.sD : nullptr;
+  TX* __restrict__ XT = a.T ? reinterpret_cast<TX*>(a.T) + (int64_t)unit * a.sT : nullptr;
 
   const int tid = threadIdx.x;
   const int cg = tid & 7;   // 8-column group
@@ -123,15 +123,17 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MomArgs a) {
         }
       }
       // own layout: row r, columns c..c+8 (columns past cols are zero padding)
-      st8(X + (int64_t)r * a.ldd + c, u);
+      if (X) st8(X + (int64_t)r * a.ldd + c, u);
     }
+    if (XT) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) tile[lr][cg * 8 + e] = u[e];
+      for (int e = 0; e < 8; ++e) tile[lr][cg * 8 + e] = u[e];
+    }
   }
   __syncthreads();
   // transposed layout: row c0 + cc, columns r0 .. r0+64: 64 rows x 8 chunks of 8
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < 2 && XT; ++j) {
     const int q = tid + 256 * j;
     const int cc = q >> 3, rq = q & 7;
     const int gc = c0 + cc, gr = r0 + rq * 8;

@@ -212,7 +212,27 @@ __device__ __forceinline__ void final8_tail(TW* w, float* o, const float (&v)[8]
   }
 }
 
-template <int BM, int BN, typename TI, typename TO, bool SYM, int EPI>
+// 4 x 16-bit transposed LDS read (ds_read_b64_tr_b16): within each group of
+// 16 lanes, lane 4e + q supplies the address of 4 consecutive elements of
+// row e, and lane L receives element L % 4 of the 4 lanes 4e + L / 4, e =
+// 0..3, i.e. column 4 (L / 4) + L % 4 = L of rows 0..3: a 4 x 16 block read
+// row-wise comes back column-wise (layout checked on the device).
+// Issued as inline assembly: the compiler's builtin for it makes every such
+// read wait for all outstanding LDS-DMA copies (it cannot tell the ring slots
+// apart), which would serialize the copies of the next stage with the reads
+// of this one.  The compiler does not track this read's completion, so the
+// caller waits (lgkmcnt) before using the result.
+__device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
+  uint2 r;
+  const uint32_t addr = (uint32_t)(uintptr_t)(lds_ptr_t)p;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+
+// s_waitcnt lgkmcnt(0) alone.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+template <int BM, int BN, typename TI, typename TO, bool SYM, int EPI, bool TRANS = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_kernel(const GemmArgs a) {
   constexpr int ES = (int)sizeof(TI);
@@ -268,6 +288,10 @@ void gemm_kernel(const GemmArgs a) {
   }
   const int row0 = bi * BM, col0 = bj * BN;
 
+  // chunk swizzle of a K-major stage: 16-bit rows k..k+3 read together by the
+  // transposed loads land 32 bytes apart; fp32 rows k and k+4 128 bytes apart
+  auto swz_t = [](int krow) { return ES == 2 ? 2 * (krow & 3) : ((krow >> 2) & 1) << 3; };
+
   // ---- copy plan: waves 0,1 copy L rows, waves 2,3 copy R rows, each wave
   // half of its operand's rows.  Copy q of a wave fills 64 consecutive slots
   // = 8 rows x 8 chunks; lane l lands in row 8q + l/8 (of the wave's half)
@@ -277,22 +301,40 @@ void gemm_kernel(const GemmArgs a) {
   const TI* P = reinterpret_cast<const TI*>(copiesL ? a.L : a.R) +
                 (int64_t)unit * (copiesL ? a.sL : a.sR);
   const int64_t ld = copiesL ? a.ldl : a.ldr;
-  const int crow = (copiesL ? row0 : col0) + (wid & 1) * (BM / 2) + (lane >> 3);  // operand row of copy 0
   const int prows = copiesL ? a.M : a.N;
-  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(P, (uint32_t)((int64_t)prows * ld * ES));
+  const int slot_off = (copiesL ? 0 : BM * CPR) + (wid & 1) * (BM / 2) * CPR;
+  // row-major operand (TRANS = false)
+  const int crow = (copiesL ? row0 : col0) + (wid & 1) * (BM / 2) + (lane >> 3);  // operand row of copy 0
   const int ck0 = ((lane & 7) ^ (lane >> 3)) * EPC;        // k of this lane's chunk, even copies
   const int ck1 = ((lane & 7) ^ (lane >> 3) ^ 1) * EPC;    // odd copies
   const uint32_t cb0 = (uint32_t)(((int64_t)crow * ld + ck0) * ES);
   const uint32_t cb1 = (uint32_t)(((int64_t)crow * ld + ck1) * ES);
   const uint32_t cstep = (uint32_t)(8 * ld * ES);
-  const int slot_off = (copiesL ? 0 : BM * CPR) + (wid & 1) * (BM / 2) * CPR;
+  // K-major operand (TRANS): element (i, k) at P[k * ld + i].  A stage of an
+  // operand is BK rows k of BM elements i, CR 16-byte chunks per row, chunk
+  // c of row k at slot k * CR + (c ^ swzT(k)); a copy instruction fills 64
+  // consecutive slots.
+  constexpr int CR = BM * ES / 16;
+  const int c0op = copiesL ? row0 : col0;
+  const __amdgpu_buffer_rsrc_t rsrc =
+      make_rsrc(P, (uint32_t)((int64_t)(TRANS ? a.K : prows) * ld * ES));
 
   auto copy_one = [&](int q, int stage) {
     const int k0 = stage * BK;
-    const int ck = (q & 1) ? ck1 : ck0;
-    const uint32_t cb = (q & 1) ? cb1 : cb0;
-    const bool ok = (k0 + ck < a.K) && (crow + 8 * q < prows);
-    const uint32_t off = ok ? cb + (uint32_t)(k0 * ES) + (uint32_t)q * cstep : OOB;
+    uint32_t off;
+    if constexpr (TRANS) {
+      const int slot = ((wid & 1) * NQ + q) * 64 + lane;
+      const int krow = slot / CR;
+      const int lc = (slot % CR) ^ swz_t(krow);
+      const int col = c0op + lc * EPC;
+      const bool ok = (k0 + krow < a.K) && (col < prows);
+      off = ok ? (uint32_t)(((int64_t)(k0 + krow) * ld + col) * ES) : OOB;
+    } else {
+      const int ck = (q & 1) ? ck1 : ck0;
+      const uint32_t cb = (q & 1) ? cb1 : cb0;
+      const bool ok = (k0 + ck < a.K) && (crow + 8 * q < prows);
+      off = ok ? cb + (uint32_t)(k0 * ES) + (uint32_t)q * cstep : OOB;
+    }
     copy16_to_lds(rsrc, &ring[stage % NSTG][slot_off + q * 64], off);
   };
 
@@ -310,13 +352,37 @@ void gemm_kernel(const GemmArgs a) {
   const int rswz = (l32 & 7) ^ ((l32 >> 3) & 1);
   auto read_one = [&](int r, int stage, int s, int slot) {
     const u32x4* st = ring[stage % NSTG];
-    const int c = (2 * s + half) ^ rswz;
-    if (r < WTM) {
-      fa[slot][r] = st[(wm * (BM / 2) + r * 32 + l32) * CPR + c];
+    const int region = r < WTM ? 0 : BM * CPR;                                    // L or R slots
+    const int rb = r < WTM ? wm * (BM / 2) + r * 32 : wn * WN + (r - WTM) * 32;  // fragment's first row
+    u32x4 v;
+    if constexpr (!TRANS) {
+      v = st[region + (rb + l32) * CPR + ((2 * s + half) ^ rswz)];
+    } else if constexpr (sizeof(TI) == 2) {
+      // 8 consecutive k (16s + 8 half + 0..7) of row rb + l32: two transposed
+      // 4 x 16 reads; lane 4e + q of each 16-lane group addresses row k + e at
+      // columns rb + 16 ((lane >> 4) & 1) + 4q
+      const int e = (lane >> 2) & 3, q = lane & 3;
+      const int col = rb + 16 * ((lane >> 4) & 1) + 4 * q;
+      const char* base = reinterpret_cast<const char*>(st + region);
+#pragma unroll
+      for (int kq = 0; kq < 2; ++kq) {
+        const int krow = 16 * s + 8 * half + 4 * kq + e;
+        const uint2 w = lds_read_tr16(base + (krow * CR + ((col >> 3) ^ swz_t(krow))) * 16 + (col & 7) * 2);
+        v[2 * kq] = w.x;
+        v[2 * kq + 1] = w.y;
+      }
     } else {
-      const int j = r - WTM;
-      fb[slot][j] = st[BM * CPR + (wn * WN + j * 32 + l32) * CPR + c];
+      // fp32: 4 consecutive k (8s + 4 half + 0..3) of row rb + l32, one load each
+      const int col = rb + l32;
+      const float* base = reinterpret_cast<const float*>(st + region);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int krow = 8 * s + 4 * half + e;
+        v[e] = __builtin_bit_cast(uint32_t, base[(krow * CR + ((col >> 2) ^ swz_t(krow))) * 4 + (col & 3)]);
+      }
     }
+    if (r < WTM) fa[slot][r] = v;
+    else fb[slot][r - WTM] = v;
   };
   auto mfma_pair = [&](int p, int slot) {
     const int i = p / WTN, j = p % WTN;
@@ -334,11 +400,16 @@ void gemm_kernel(const GemmArgs a) {
 #pragma unroll
   for (int r = 0; r < NDR; ++r) read_one(r, 0, 0, 0);
 
+  // transposed 16-bit reads are not tracked by the compiler: wait for them
+  // explicitly before the MFMAs of the step they feed
+  constexpr bool kManualLgkm = TRANS && sizeof(TI) == 2;
   for (int kt = 0; kt < nk; ++kt) {
     __builtin_amdgcn_sched_barrier(0);
     // steps 0 .. NSTEP-2: MFMAs on the fragments in registers, reads of the next step
 #pragma unroll
     for (int s = 0; s + 1 < NSTEP; ++s) {
+      if constexpr (kManualLgkm) wait_lgkm0();
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int p = 0; p < NPAIR; ++p) {
         mfma_pair(p, s & 1);
@@ -351,6 +422,7 @@ void gemm_kernel(const GemmArgs a) {
     // stage kt's slot may be refilled
     wait_vmcnt_lgkm0<0>();
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
     // last step: copies of stage kt+2 into the freed slot, fragment reads of
     // step 0 of stage kt+1
 #pragma unroll
@@ -365,8 +437,8 @@ void gemm_kernel(const GemmArgs a) {
   }
 
   // ---------------------------------------------------------------- epilogue
-  wait_vmcnt<0>();  // the trailing (zero) copies have landed
-  __syncthreads();                      // every wave is done with the ring
+  wait_vmcnt_lgkm0<0>();  // the trailing (zero) copies and fragment reads are done
+  __syncthreads();        // every wave is done with the ring
   float alpha = a.alpha;
   if (a.alphaSel != SEL_ONE) {
     const float4 ax = a.aux[unit];

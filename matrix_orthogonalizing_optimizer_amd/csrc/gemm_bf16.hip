@@ -5,26 +5,29 @@
 namespace muon {
 
 namespace {
-template <int T, typename TO, bool SYM, int EPI>
+template <int T, typename TO, bool SYM, int EPI, bool TRANS = false>
 hipError_t go(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<T, T, bf16, TO, SYM, EPI>), dim3(a.totalTiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<T, T, bf16, TO, SYM, EPI, TRANS>), dim3(a.totalTiles), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 template <int T>
-hipError_t dispatch(int to, bool sym, int epi, const GemmArgs& a, hipStream_t s) {
-  if (sym && epi == EPI_SCALE && to == DT_BF16) return go<T, bf16, true, EPI_SCALE>(a, s);
-  if (sym && epi == EPI_SCALE && to == DT_F16) return go<T, f16, true, EPI_SCALE>(a, s);
-  if (sym && epi == EPI_POLY && to == DT_BF16) return go<T, bf16, true, EPI_POLY>(a, s);
-  if (!sym && epi == EPI_AXPY && to == DT_BF16) return go<T, bf16, false, EPI_AXPY>(a, s);
-  if (!sym && epi == EPI_FINAL && to == DT_BF16) return go<T, bf16, false, EPI_FINAL>(a, s);
-  if (!sym && epi == EPI_FINAL && to == DT_F32) return go<T, float, false, EPI_FINAL>(a, s);
+hipError_t dispatch(int to, bool sym, int epi, bool trans, const GemmArgs& a, hipStream_t s) {
+  if (!trans && sym && epi == EPI_SCALE && to == DT_BF16) return go<T, bf16, true, EPI_SCALE>(a, s);
+  if (!trans && sym && epi == EPI_SCALE && to == DT_F16) return go<T, f16, true, EPI_SCALE>(a, s);
+  if (!trans && sym && epi == EPI_POLY && to == DT_BF16) return go<T, bf16, true, EPI_POLY>(a, s);
+  if (!trans && !sym && epi == EPI_AXPY && to == DT_BF16) return go<T, bf16, false, EPI_AXPY>(a, s);
+  if (!trans && !sym && epi == EPI_FINAL && to == DT_BF16) return go<T, bf16, false, EPI_FINAL>(a, s);
+  if (!trans && !sym && epi == EPI_FINAL && to == DT_F32) return go<T, float, false, EPI_FINAL>(a, s);
+  // K-major operands (A = Y^T Y from the transposed copy)
+  if (trans && sym && epi == EPI_SCALE && to == DT_BF16) return go<T, bf16, true, EPI_SCALE, true>(a, s);
+  if (trans && sym && epi == EPI_SCALE && to == DT_F16) return go<T, f16, true, EPI_SCALE, true>(a, s);
   return hipErrorInvalidValue;
 }
 }  // namespace
 
-hipError_t launch_gemm_bf16(int tile, int to, bool sym, int epi, const GemmArgs& a, hipStream_t s) {
-  return tile == 256 ? dispatch<256>(to, sym, epi, a, s) : dispatch<128>(to, sym, epi, a, s);
+hipError_t launch_gemm_bf16(int tile, int to, bool sym, int epi, bool trans, const GemmArgs& a, hipStream_t s) {
+  return tile == 256 ? dispatch<256>(to, sym, epi, trans, a, s) : dispatch<128>(to, sym, epi, trans, a, s);
 }
 
 }  // namespace muon

@@ -32,8 +32,8 @@ struct GemmArgs {
 // Momentum kernel (see elementwise.hpp).
 struct MomArgs {
   const UnitDesc* desc;
-  void* D;         // U in the parameter's own layout (rows x cols)
-  void* T;         // U transposed (cols x rows)
+  void* D;         // U in the parameter's own layout (rows x cols), or null
+  void* T;         // U transposed (cols x rows), or null
   int64_t ldd, ldt;  // leading dimensions (multiples of 8)
   int64_t sD, sT;    // per-unit element strides
   float* partials; // one per workgroup

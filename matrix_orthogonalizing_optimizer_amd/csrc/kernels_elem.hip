@@ -4,12 +4,12 @@
 
 namespace muon {
 
-hipError_t launch_gemm(int tile, int ti, int to, bool sym, int epi, const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm(int tile, int ti, int to, bool sym, int epi, bool trans, const GemmArgs& a, hipStream_t s) {
   if (a.totalTiles <= 0) return hipSuccess;
   switch (ti) {
-    case DT_BF16: return launch_gemm_bf16(tile, to, sym, epi, a, s);
-    case DT_F16: return launch_gemm_f16(tile, to, sym, epi, a, s);
-    case DT_F32: return launch_gemm_f32(tile, to, sym, epi, a, s);
+    case DT_BF16: return launch_gemm_bf16(tile, to, sym, epi, trans, a, s);
+    case DT_F16: return launch_gemm_f16(tile, to, sym, epi, trans, a, s);
+    case DT_F32: return launch_gemm_f32(tile, to, sym, epi, trans, a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -8,12 +8,13 @@
 namespace muon {
 
 // GEMM launch for input dtype ti / output dtype to (DT_*), tile edge 128 or
-// 256, symmetric-output flag and epilogue kind.  Returns
+// 256, symmetric-output flag, epilogue kind and operand layout (trans: both
+// operands K-major, element (i, k) at p[k * ld + i]).  Returns
 // hipErrorInvalidValue for a combination that is not instantiated.
-hipError_t launch_gemm(int tile, int ti, int to, bool sym, int epi, const GemmArgs& a, hipStream_t s);
-hipError_t launch_gemm_bf16(int tile, int to, bool sym, int epi, const GemmArgs& a, hipStream_t s);
-hipError_t launch_gemm_f16(int tile, int to, bool sym, int epi, const GemmArgs& a, hipStream_t s);
-hipError_t launch_gemm_f32(int tile, int to, bool sym, int epi, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm(int tile, int ti, int to, bool sym, int epi, bool trans, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_bf16(int tile, int to, bool sym, int epi, bool trans, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_f16(int tile, int to, bool sym, int epi, bool trans, const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm_f32(int tile, int to, bool sym, int epi, bool trans, const GemmArgs& a, hipStream_t s);
 
 hipError_t launch_momentum(int gdtype, int xdtype, bool tall, const MomArgs& a, int64_t blocks,
                            hipStream_t s);

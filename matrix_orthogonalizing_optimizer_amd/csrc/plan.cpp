@@ -29,24 +29,22 @@ int32_t resolve_method(int32_t method, int64_t m, int64_t n) {
 bool bucket_addressable(const PlanBucket& b) {
   // every GEMM operand of one unit is addressed with 32-bit byte offsets
   const uint64_t es = (uint64_t)elem_size(b.cdtype);
-  const uint64_t lim = uint64_t(1) << 31;
-  return (uint64_t)b.m * (uint64_t)b.ldx * es < lim && (uint64_t)b.n * (uint64_t)b.mp * es < lim;
+  return (uint64_t)b.n * (uint64_t)b.mp * es < (uint64_t(1) << 31);
 }
 
-// Per unit: X (m x ldx, the wide orientation), Y = X^T (n x mp); standard
-// method: X, Y0, Y1, A, B (A, B m x mp); Gram: X0, Y0, R, T and three P / Z
-// buffers (m x mp each, fp16 for a bf16 bucket).
+// Per unit: Y = X^T (n x mp), the transposed copy of the unit kept through the
+// iteration (the symmetric products read it K-major); standard method: Y0,
+// Y1, A, P; Gram: Y0, R, T and three P / Z buffers (m x mp each, fp16 for a
+// bf16 bucket).
 size_t per_unit_data_bytes(const PlanBucket& b) {
   const size_t es = (size_t)elem_size(b.cdtype);
-  const size_t xb = (size_t)b.m * (size_t)b.ldx * es;
   const size_t yb = (size_t)b.n * (size_t)b.mp * es;
   const size_t sb = (size_t)b.m * (size_t)b.mp * es;
-  if (b.method == MUON_NS_GRAM) return xb + yb + 5 * sb;
-  return xb + 2 * yb + 2 * sb;
+  if (b.method == MUON_NS_GRAM) return yb + 5 * sb;
+  return 2 * yb + 2 * sb;
 }
 
 void bucket_derive(PlanBucket& b, size_t chunk_cap_bytes) {
-  b.ldx = round_up(b.n, 8);
   b.mp = round_up(b.m, 8);
   b.tile = b.m <= 192 ? 128 : 256;
   // momentum kernel tiles over the unit in parameter layout
@@ -57,19 +55,17 @@ void bucket_derive(PlanBucket& b, size_t chunk_cap_bytes) {
   chunk = std::max<int64_t>(1, std::min<int64_t>(chunk, b.count));
   b.chunk = (int32_t)chunk;
   const size_t es = (size_t)elem_size(b.cdtype);
-  const size_t xb = align_ws((size_t)chunk * b.m * b.ldx * es);
   const size_t yb = align_ws((size_t)chunk * b.n * b.mp * es);
   const size_t sb = align_ws((size_t)chunk * b.m * b.mp * es);
   size_t o = 0;
   for (int i = 0; i < 8; ++i) b.off[i] = 0;
-  b.off[0] = o; o += xb;
-  b.off[1] = o; o += yb;
+  b.off[0] = o; o += yb;
   if (b.method == MUON_NS_GRAM) {
-    for (int i = 2; i < 7; ++i) { b.off[i] = o; o += sb; }
+    for (int i = 1; i < 6; ++i) { b.off[i] = o; o += sb; }
   } else {
-    b.off[2] = o; o += yb;
+    b.off[1] = o; o += yb;
+    b.off[2] = o; o += sb;
     b.off[3] = o; o += sb;
-    b.off[4] = o; o += sb;
   }
   b.data_bytes = o;
 }

@@ -25,10 +25,9 @@ struct PlanBucket {
   int32_t first, count;  // range in the bucket-ordered unit list
   int32_t chunk;         // units per chunk
   int32_t tile;          // GEMM tile edge (128 or 256)
-  int64_t ldx;           // leading dimension of m x n matrices (round_up(n, 8))
-  int64_t mp;            // leading dimension of m x m matrices (round_up(m, 8))
+  int64_t mp;            // leading dimension of every workspace matrix (round_up(m, 8))
   int32_t km_tiles;      // momentum-kernel workgroups per unit
-  size_t off[8];         // data sub-buffers: standard X Y0 Y1 A B; gram X0 Y0 R T PZ0 PZ1 PZ2
+  size_t off[8];         // data sub-buffers: standard Y0 Y1 A B; gram Y0 R T PZ0 PZ1 PZ2
   size_t data_bytes;     // per chunk
 };
 
@@ -52,7 +51,7 @@ struct PlanImpl {
 int64_t round_up(int64_t x, int64_t m);
 int32_t elem_size(int32_t cdtype);
 void bucket_derive(PlanBucket& b, size_t chunk_cap_bytes);
-bool bucket_addressable(const PlanBucket& b);  // one unit's m x n operand < 2^31 bytes
+bool bucket_addressable(const PlanBucket& b);  // one unit's n x m operand < 2^31 bytes
 int32_t resolve_method(int32_t method, int64_t m, int64_t n);  // MUON_NS_AUTO -> standard or Gram
 size_t per_unit_data_bytes(const PlanBucket& b);
 
