@@ -229,6 +229,28 @@ __device__ __forceinline__ uint2 lds_read_tr16(const void* p) {
   return r;
 }
 
+// The same with a constant byte offset: step kstep (0..7) of a K-major stage
+// whose rows are ROWB bytes apart reads rows 16 (kstep / 2) + 4 (kstep % 2)
+// further on, folded into the instruction's offset field.
+template <int OFF> __device__ __forceinline__ uint2 lds_read_tr16_off(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  uint2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int ROWB> __device__ __forceinline__ uint2 lds_read_tr16_step(uint32_t addr, int kstep) {
+  switch (kstep) {
+    case 0: return lds_read_tr16_off<0 * ROWB>(addr);
+    case 1: return lds_read_tr16_off<4 * ROWB>(addr);
+    case 2: return lds_read_tr16_off<16 * ROWB>(addr);
+    case 3: return lds_read_tr16_off<20 * ROWB>(addr);
+    case 4: return lds_read_tr16_off<32 * ROWB>(addr);
+    case 5: return lds_read_tr16_off<36 * ROWB>(addr);
+    case 6: return lds_read_tr16_off<48 * ROWB>(addr);
+    default: return lds_read_tr16_off<52 * ROWB>(addr);
+  }
+}
+
 // s_waitcnt lgkmcnt(0) alone.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
@@ -288,9 +310,14 @@ void gemm_kernel(const GemmArgs a) {
   }
   const int row0 = bi * BM, col0 = bj * BN;
 
-  // chunk swizzle of a K-major stage: 16-bit rows k..k+3 read together by the
-  // transposed loads land 32 bytes apart; fp32 rows k and k+4 128 bytes apart
-  auto swz_t = [](int krow) { return ES == 2 ? 2 * (krow & 3) : ((krow >> 2) & 1) << 3; };
+  // chunk swizzle of a K-major stage.  16-bit: the transposed loads of 32
+  // lanes read rows k..k+3 (k a multiple of 4) at 4 consecutive chunks each;
+  // XOR with (0, 4, 10, 14)[k & 3] puts those 16 chunks on distinct 16-byte
+  // bank groups of a 256-byte LDS cycle, and each 16-lane half on distinct
+  // groups of a 128-byte one.  fp32: rows k and k+4 128 bytes apart.
+  auto swz_t = [](int krow) {
+    return ES == 2 ? (((krow & 1) << 2) ^ (((krow >> 1) & 1) * 10)) : ((krow >> 2) & 1) << 3;
+  };
 
   // ---- copy plan: waves 0,1 copy L rows, waves 2,3 copy R rows, each wave
   // half of its operand's rows.  Copy q of a wave fills 64 consecutive slots
@@ -350,6 +377,24 @@ void gemm_kernel(const GemmArgs a) {
   // fragment rows start at multiples of 32, so swz(row) depends on l32 only
   u32x4 fa[2][WTM], fb[2][WTN];
   const int rswz = (l32 & 7) ^ ((l32 >> 3) & 1);
+  // K-major 16-bit: per-lane LDS byte address of fragment r's first
+  // transposed read in stage slot 0 (lane 4e + q of each 16-lane group
+  // addresses row 8 half + e at columns rb + 16 ((lane >> 4) & 1) + 4q; the
+  // swizzle depends on the row only through e)
+  constexpr int ROWB = CR * 16;
+  uint32_t tbase[NDR];
+  if constexpr (TRANS && sizeof(TI) == 2) {
+    const int e = (lane >> 2) & 3, q = lane & 3;
+    const uint32_t ring0 = (uint32_t)(uintptr_t)(lds_ptr_t)&ring[0][0];
+#pragma unroll
+    for (int r = 0; r < NDR; ++r) {
+      const int region = r < WTM ? 0 : BM * CPR;
+      const int rb = r < WTM ? wm * (BM / 2) + r * 32 : wn * WN + (r - WTM) * 32;
+      const int col = rb + 16 * ((lane >> 4) & 1) + 4 * q;
+      tbase[r] = ring0 + (uint32_t)(region * 16 + (8 * half + e) * ROWB + ((col >> 3) ^ swz_t(e)) * 16 +
+                                    (col & 7) * 2);
+    }
+  }
   auto read_one = [&](int r, int stage, int s, int slot) {
     const u32x4* st = ring[stage % NSTG];
     const int region = r < WTM ? 0 : BM * CPR;                                    // L or R slots
@@ -359,15 +404,11 @@ void gemm_kernel(const GemmArgs a) {
       v = st[region + (rb + l32) * CPR + ((2 * s + half) ^ rswz)];
     } else if constexpr (sizeof(TI) == 2) {
       // 8 consecutive k (16s + 8 half + 0..7) of row rb + l32: two transposed
-      // 4 x 16 reads; lane 4e + q of each 16-lane group addresses row k + e at
-      // columns rb + 16 ((lane >> 4) & 1) + 4q
-      const int e = (lane >> 2) & 3, q = lane & 3;
-      const int col = rb + 16 * ((lane >> 4) & 1) + 4 * q;
-      const char* base = reinterpret_cast<const char*>(st + region);
+      // 4 x 16 reads, rows 16s + 4kq further on than the base address
+      const uint32_t a0 = tbase[r] + (uint32_t)((stage % NSTG) * STG * 16);
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq) {
-        const int krow = 16 * s + 8 * half + 4 * kq + e;
-        const uint2 w = lds_read_tr16(base + (krow * CR + ((col >> 3) ^ swz_t(krow))) * 16 + (col & 7) * 2);
+        const uint2 w = lds_read_tr16_step<ROWB>(a0, 2 * s + kq);
         v[2 * kq] = w.x;
         v[2 * kq + 1] = w.y;
       }

@@ -12,8 +12,8 @@ namespace muon {
 
 namespace {
 
-const char* kNames[F_COUNT] = {"momentum_norm", "norm_finalize", "ns_gram_xxt", "ns_poly_bA_cAA",
-                               "ns_update_aX_BX", "ns_final_update", "gram_r0", "gram_p",
+const char* kNames[F_COUNT] = {"momentum_norm", "norm_finalize", "ns_gram_A", "ns_poly_P",
+                               "ns_update_PX", "ns_final_update", "gram_r0", "gram_p",
                                "gram_q", "gram_t", "gram_r", "adamw"};
 
 struct Rec {
