@@ -286,12 +286,26 @@ void gemm_kernel(const GemmArgs a) {
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  // ---- workgroup -> (unit, tile): XCD-contiguous ranges of logical tiles
+  // ---- workgroup -> (unit, tile).  Workgroup b runs on XCD b & 7.  Logical
+  // tiles are dealt to the XCDs in chunks of S consecutive tiles, chunk c to
+  // XCD c & 7: at any time the 8 XCDs work on neighbouring chunks (mostly one
+  // unit, whose operands then stay in the Infinity Cache), and the ~32 tiles an
+  // XCD runs at once lie in one chunk (operand bands shared through its L2).
+  // S: 32 upper-triangle tiles, or two 4-row groups of a non-symmetric
+  // product (measured best of 16..272).  The tail short of a full round of 8
+  // chunks is split into 8 contiguous ranges, so the map stays a bijection.
   int logical;
   {
     const int b = blockIdx.x, tot = a.totalTiles;
-    const int xcd = b & 7, loc = b >> 3, q = tot >> 3, r = tot & 7;
-    logical = xcd * q + (xcd < r ? xcd : r) + loc;
+    const int xcd = b & 7, loc = b >> 3;
+    const int S = SYM ? 32 : 8 * a.tilesN;
+    const int full = tot / (8 * S);
+    if (loc < full * S) {
+      logical = (loc / S) * 8 * S + xcd * S + loc % S;
+    } else {
+      const int rest = tot - full * 8 * S, q = rest >> 3, r = rest & 7;
+      logical = full * 8 * S + xcd * q + (xcd < r ? xcd : r) + (loc - full * S);
+    }
   }
   const int unit = logical / a.tilesPerUnit;
   const int tt = logical - unit * a.tilesPerUnit;
