@@ -167,7 +167,7 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
       if (k + 1 < cp.steps) {
         g.C = Y[(k + 1) & 1]; g.ldc = b.mp; g.sC = sy;
         HIP_TRY(timed(F_UPDATE, mm_n, 0.0, st,
-                      [&] { return launch_gemm(T, cdt, cdt, false, EPI_AXPY, false, g, st); }));
+                      [&] { return launch_gemm(T, cdt, cdt, false, EPI_SCALE, false, g, st); }));
       } else {
         final_args(g);
         HIP_TRY(timed(F_FINAL, mm_n, elems * 2.0 * pes, st,
@@ -223,7 +223,7 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
         g.C = PZ[zn]; g.ldc = b.mp; g.sC = ss;
       }
       HIP_TRY(timed(F_GRAM_Q, mmm, 0.0, st,
-                    [&] { return launch_gemm(T, sdt, last ? qdt_last : sdt, false, EPI_AXPY, false, g, st); }));
+                    [&] { return launch_gemm(T, sdt, last ? qdt_last : sdt, false, EPI_SCALE, false, g, st); }));
       z = zn;
     }
     if (!last) {
@@ -234,7 +234,7 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
       g.C = Tm; g.ldc = b.mp; g.sC = ss;
       g.beta = 0.f;
       HIP_TRY(timed(F_GRAM_T, mmm, 0.0, st,
-                    [&] { return launch_gemm(T, sdt, sdt, false, EPI_AXPY, false, g, st); }));
+                    [&] { return launch_gemm(T, sdt, sdt, false, EPI_SCALE, false, g, st); }));
       // R = Tm P  (P symmetric; the result is symmetric: upper tiles + mirror)
       g = sym_args(Tm, b.mp, ss, PZ[p], b.mp, ss, (int)m, R);
       HIP_TRY(timed(F_GRAM_R, mmm, 0.0, st,

@@ -55,6 +55,20 @@ template <> __device__ __forceinline__ float from_f32<float>(float x) { return x
 __device__ __forceinline__ uint16_t bits16(bf16 x) { return __builtin_bit_cast(uint16_t, x); }
 __device__ __forceinline__ uint16_t bits16(f16 x) { return __builtin_bit_cast(uint16_t, x); }
 
+// Two floats -> two 16-bit values of T in one 32-bit word (a in the low
+// half), one v_cvt_pk_{bf16,f16}_f32, rounding to nearest even as the
+// element-wise conversion does.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+template <typename T> __device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (__is_same(T, bf16)) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+  }
+}
+
 // Deterministic wave64 sum (fixed butterfly order).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

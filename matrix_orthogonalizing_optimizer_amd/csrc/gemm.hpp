@@ -140,12 +140,27 @@ template <typename T> __device__ __forceinline__ void store8(T* p, const float (
   if constexpr (sizeof(T) == 2) {
     u32x4 w;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      w[j] = (uint32_t)bits16(from_f32<T>(v[2 * j])) | ((uint32_t)bits16(from_f32<T>(v[2 * j + 1])) << 16);
+    for (int j = 0; j < 4; ++j) w[j] = pack2<T>(v[2 * j], v[2 * j + 1]);
     *reinterpret_cast<u32x4*>(p) = w;
   } else {
     *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
     *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  }
+}
+
+// 8 consecutive elements of T stored through a buffer resource at byte
+// offset off; an offset at or past the resource's size drops the store.
+template <typename T>
+__device__ __forceinline__ void buffer_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = pack2<T>(v[2 * j], v[2 * j + 1]);
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, 0);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{v[0], v[1], v[2], v[3]}), r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{v[4], v[5], v[6], v[7]}), r,
+                                           off + 16, 0, 0);
   }
 }
 
@@ -307,8 +322,11 @@ void gemm_kernel(const GemmArgs a) {
       logical = full * 8 * S + xcd * q + (xcd < r ? xcd : r) + (loc - full * S);
     }
   }
-  const int unit = logical / a.tilesPerUnit;
-  const int tt = logical - unit * a.tilesPerUnit;
+  // the division runs on the vector unit: bring the (uniform) results back
+  // to scalar registers, or every buffer resource built from them would be
+  // treated as divergent
+  const int unit = __builtin_amdgcn_readfirstlane(logical / a.tilesPerUnit);
+  const int tt = __builtin_amdgcn_readfirstlane(logical - unit * a.tilesPerUnit);
   int bi, bj;
   if constexpr (SYM) {
     upper_tile(tt, a.tilesM, bi, bj);
@@ -322,6 +340,8 @@ void gemm_kernel(const GemmArgs a) {
     bi = first + w % gm;
     bj = w / gm;
   }
+  bi = __builtin_amdgcn_readfirstlane(bi);
+  bj = __builtin_amdgcn_readfirstlane(bj);
   const int row0 = bi * BM, col0 = bj * BN;
 
   // chunk swizzle of a K-major stage.  16-bit: the transposed loads of 32
@@ -502,6 +522,11 @@ void gemm_kernel(const GemmArgs a) {
   const TI* Ep = reinterpret_cast<const TI*>(a.E) + (int64_t)unit * a.sE;
   TO* Cp = a.C ? reinterpret_cast<TO*>(a.C) + (int64_t)unit * a.sC : nullptr;
   TO* C2p = a.C2 ? reinterpret_cast<TO*>(a.C2) + (int64_t)unit * a.sC2 : nullptr;
+  // buffer resources of the outputs and the addend: a store at or past the
+  // end is dropped, a load there returns zeros
+  const __amdgpu_buffer_rsrc_t crs = make_rsrc(Cp, (uint32_t)((int64_t)a.M * a.ldc * (int64_t)sizeof(TO)));
+  const __amdgpu_buffer_rsrc_t c2rs = make_rsrc(C2p, (uint32_t)((int64_t)a.N * a.ldc2 * (int64_t)sizeof(TO)));
+  const __amdgpu_buffer_rsrc_t ers = make_rsrc(Ep, (uint32_t)((int64_t)a.M * a.lde * ES));
 
   float keep = 1.f, step = 0.f;
   UnitDesc d;
@@ -516,52 +541,58 @@ void gemm_kernel(const GemmArgs a) {
   // a tall unit's parameter block has that layout, a wide unit's the transposed one
   const bool fdirect = EPI == EPI_FINAL && a.tall;
   const bool fmirror = EPI == EPI_FINAL && !a.tall;
-  const bool use_e = EPI == EPI_POLY || a.beta != 0.f;  // AXPY and FINAL: beta E + L R^T
   const bool wpre = EPI == EPI_FINAL && !store_only && a.wvec != 0;
+  const bool mirror = EPI == EPI_FINAL ? fmirror : C2p != nullptr;
   float* strip = reinterpret_cast<float*>(&ring[0][0]) + wid * (32 * SROW);
+  const int gc0 = col0 + wn * WN;  // global column of strip column 0
 
-  // Each pass covers the 32 x WN strip in NT rounds of 64 lanes x 8 elements:
-  // the direct pass by strip rows (r, c8..c8+7), the mirror pass by strip
-  // columns (c8..c8+7 of column jj).
+  // Each pass covers the 32 x WN strip of MFMA row-tile i in NT rounds of 64
+  // lanes x 8 elements.  Direct pass: with CW = WN / 8 chunks per strip row,
+  // lane l covers rows l / CW + (64 / CW) t at columns 8 (l % CW) .. +7.
+  // Mirror pass: strip column jj = (64 t + l) % WN, rows c8 .. c8 + 7 with
+  // c8 = 8 ((64 t + l) / WN).
   constexpr int NT = 32 * WN / 8 / 64;
-  auto dpos = [&](int t, int& r, int& c8) {
-    const int q = t * 64 + lane;
-    r = q / (WN / 8);
-    c8 = (q % (WN / 8)) * 8;
-  };
+  constexpr int CW = WN / 8, DRS = 64 / CW;
+  static_assert(64 % CW == 0 && NT * DRS == 32, "direct pass covers the strip");
+  const int dr0 = lane / CW, dc8 = (lane % CW) * 8;
+  const int gj = gc0 + dc8;  // direct pass: this lane's first output column
   auto mpos = [&](int t, int& jj, int& c8) {
     const int q = t * 64 + lane;
     jj = q % WN;
     c8 = (q / WN) * 8;
   };
 
+  // EPI_POLY's addend E at the direct-pass positions of strip i, as
+  // unconditional buffer loads (pieces past column N get an out-of-range
+  // offset).  Strip i + 1's loads are issued before strip i's stores, so
+  // waiting for them never waits for a store.
+  Raw8<TI> pe[2][NT];
+  auto load_e = [&](int i, Raw8<TI>(&dst)[NT]) {
+    const uint32_t estep = (uint32_t)(DRS * a.lde * ES);
+    uint32_t off = gj < a.N ? (uint32_t)(((int64_t)(row0 + wm * (BM / 2) + i * 32 + dr0) * a.lde + gj) * ES) : OOB;
+#pragma unroll
+    for (int t = 0; t < NT; ++t, off += estep) {
+#pragma unroll
+      for (int h = 0; h < (int)(ES / 2); ++h) dst[t].w[h] = __builtin_amdgcn_raw_buffer_load_b128(ers, off + 16 * h, 0, 0);
+    }
+  };
+  if constexpr (EPI == EPI_POLY) load_e(0, pe[0]);
+
 #pragma unroll
   for (int i = 0; i < WTM; ++i) {
     const int gr0 = row0 + wm * (BM / 2) + i * 32;  // global row of strip row 0
-    const int gc0 = col0 + wn * WN;                 // global column of strip column 0
 
-    // this strip's global loads go out first: the addend E (direct pass
-    // positions) and, for the fused update, the old parameter values
-    // (positions of the pass that writes them)
-    Raw8<TI> pe[NT];
+    // the fused update's old parameter values (positions of the pass that
+    // writes them) go out before this strip's LDS work
     Raw8<TO> pw[NT];
+    if constexpr (EPI == EPI_FINAL) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      raw_zero(pe[t]);
-      if constexpr (EPI != EPI_SCALE) {
-        int r, c8;
-        dpos(t, r, c8);
-        const int gi = gr0 + r, gj = gc0 + c8;
-        if (use_e && gi < a.M && gj < a.N) raw_load8(Ep + (int64_t)gi * a.lde + gj, pe[t]);
-      }
-      if constexpr (EPI == EPI_FINAL) {
+      for (int t = 0; t < NT; ++t) {
         raw_zero(pw[t]);
         int pr, pc;  // parameter row, first column
         if (fdirect) {
-          int r, c8;
-          dpos(t, r, c8);
-          pr = gr0 + r;
-          pc = gc0 + c8;
+          pr = gr0 + dr0 + DRS * t;
+          pc = gj;
         } else {
           int jj, c8;
           mpos(t, jj, c8);
@@ -595,81 +626,124 @@ void gemm_kernel(const GemmArgs a) {
       else final8_tail(w, o, v, nv, keep, step, store_only);
     };
 
-    // direct pass: output values in place, stored as rows when requested
+    // direct pass: all NT pieces are read before any is used, turned into
+    // output values, written back when the mirror pass needs them, and
+    // stored as 16-byte row chunks
+    float v[NT][8];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      int r, c8;
-      dpos(t, r, c8);
-      const int gi = gr0 + r, gj = gc0 + c8;
-      float* sp = strip + r * SROW + c8;
-      float v[8];
-      {
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(sp);
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(sp + 4);
+      const float* sp = strip + (dr0 + DRS * t) * SROW + dc8;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(sp);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(sp + 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { v[e] = lo[e]; v[e + 4] = hi[e]; }
-      }
-      const bool inb = gi < a.M && gj < a.N;  // 8-chunks end inside the ld padding
-      if constexpr (EPI == EPI_SCALE) {
+      for (int e = 0; e < 4; ++e) { v[t][e] = lo[e]; v[t][e + 4] = hi[e]; }
+    }
+    if constexpr (EPI == EPI_POLY) {
+      if (i + 1 < WTM) load_e(i + 1, pe[(i + 1) & 1]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] *= alpha;
-      } else if constexpr (EPI == EPI_POLY) {
+      for (int t = 0; t < NT; ++t) {
+        const int gi = gr0 + dr0 + DRS * t;
         float e8[8];
-        raw_unpack8(pe[t], e8);
+        raw_unpack8(pe[i & 1][t], e8);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = alpha * v[e] + a.beta * e8[e] + (gi == gj + e ? a.gamma : 0.f);
-      } else {
-        float e8[8];
-        raw_unpack8(pe[t], e8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = alpha * (a.beta * e8[e] + v[e]);
+        for (int e = 0; e < 8; ++e)
+          v[t][e] = alpha * v[t][e] + a.beta * e8[e] + (gi == gj + e ? a.gamma : 0.f);
       }
-      *reinterpret_cast<f32x4*>(sp) = f32x4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<f32x4*>(sp + 4) = f32x4{v[4], v[5], v[6], v[7]};
-      if constexpr (EPI == EPI_FINAL) {
-        if (fdirect && inb) final8(pw[t], gi, gj, a.N, v);
-      } else {
-        if (Cp && inb) {
-          TO* dst = Cp + (int64_t)gi * a.ldc + gj;
-          if (!diag || gi <= gj) {
-            store8(dst, v);
-          } else if (gi < gj + 8) {
-            // diagonal tile: the upper triangle (column >= row) is stored
+    } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (gi <= gj + e) dst[e] = from_f32<TO>(v[e]);
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[t][e] *= alpha;
+    }
+    if (mirror) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float* sp = strip + (dr0 + DRS * t) * SROW + dc8;
+        *reinterpret_cast<f32x4*>(sp) = f32x4{v[t][0], v[t][1], v[t][2], v[t][3]};
+        *reinterpret_cast<f32x4*>(sp + 4) = f32x4{v[t][4], v[t][5], v[t][6], v[t][7]};
+      }
+    }
+    if constexpr (EPI == EPI_FINAL) {
+      if (fdirect && gj < a.N) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int gi = gr0 + dr0 + DRS * t;
+          if (gi < a.M) final8(pw[t], gi, gj, a.N, v[t]);
+        }
+      }
+    } else if (Cp) {
+      if (!diag) {
+        // rows at or past M fall outside the resource; pieces starting at or
+        // past N (beyond the row's padding) get an out-of-range offset
+        const uint32_t rstep = (uint32_t)(DRS * a.ldc * (int64_t)sizeof(TO));
+        uint32_t off = gj < a.N ? (uint32_t)(((int64_t)(gr0 + dr0) * a.ldc + gj) * (int64_t)sizeof(TO)) : OOB;
+#pragma unroll
+        for (int t = 0; t < NT; ++t, off += rstep) buffer_store8<TO>(crs, off, v[t]);
+      } else {
+        // diagonal tile: the upper triangle (column >= row) is stored
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int gi = gr0 + dr0 + DRS * t;
+          if (gi < a.M && gj < a.N && gi < gj + 8) {
+            TO* dst = Cp + (int64_t)gi * a.ldc + gj;
+            if (gi <= gj) {
+              store8(dst, v[t]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (gi <= gj + e) dst[e] = from_f32<TO>(v[t][e]);
+            }
           }
         }
       }
     }
 
     // mirror pass: strip column jj, rows c8..c8+7 -> row gc0 + jj of the
-    // transposed output
-    const bool mirror = EPI == EPI_FINAL ? fmirror : C2p != nullptr;
+    // transposed output (rows of the output are the tile's columns, its
+    // columns the tile's rows); all reads first, then the stores
     if (mirror) {
       __syncthreads();  // values of the direct pass are in the strip
+      float mv[NT][8];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         int jj, c8;
         mpos(t, jj, c8);
-        const int gj = gc0 + jj;  // output row
-        const int gi = gr0 + c8;  // first output column
-        float v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = strip[(c8 + e) * SROW + jj];
-        // rows of the output are the tile's columns (< N), its columns the tile's rows
-        if (gj < a.N && gi < a.M) {
-          if constexpr (EPI == EPI_FINAL) {
-            final8(pw[t], gj, gi, a.M, v);  // wide unit: parameter row gj, columns gi..
-          } else {
-            TO* dst = C2p + (int64_t)gj * a.ldc2 + gi;
-            if (!diag || gi + 7 < gj) {
-              store8(dst, v);
+        for (int e = 0; e < 8; ++e) mv[t][e] = strip[(c8 + e) * SROW + jj];
+      }
+      if constexpr (EPI == EPI_FINAL) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          int jj, c8;
+          mpos(t, jj, c8);
+          const int orow = gc0 + jj, ocol = gr0 + c8;
+          if (orow < a.N && ocol < a.M) final8(pw[t], orow, ocol, a.M, mv[t]);  // wide unit: parameter row orow
+        }
+      } else if (!diag) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          int jj, c8;
+          mpos(t, jj, c8);
+          const int orow = gc0 + jj, ocol = gr0 + c8;
+          // rows at or past N fall outside the resource
+          const uint32_t off = ocol < a.M ? (uint32_t)(((int64_t)orow * a.ldc2 + ocol) * (int64_t)sizeof(TO)) : OOB;
+          buffer_store8<TO>(c2rs, off, mv[t]);
+        }
+      } else {
+        // diagonal tile of a symmetric product: strictly lower positions
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          int jj, c8;
+          mpos(t, jj, c8);
+          const int orow = gc0 + jj, ocol = gr0 + c8;
+          if (orow < a.N && ocol < a.M) {
+            TO* dst = C2p + (int64_t)orow * a.ldc2 + ocol;
+            if (ocol + 7 < orow) {
+              store8(dst, mv[t]);
             } else {
-              // diagonal tile of a symmetric product: strictly lower positions
 #pragma unroll
               for (int e = 0; e < 8; ++e)
-                if (gi + e < gj) dst[e] = from_f32<TO>(v[e]);
+                if (ocol + e < orow) dst[e] = from_f32<TO>(mv[t][e]);
             }
           }
         }

@@ -16,7 +16,7 @@ hipError_t dispatch(int to, bool sym, int epi, bool trans, const GemmArgs& a, hi
   if (!trans && sym && epi == EPI_SCALE && to == DT_BF16) return go<T, bf16, true, EPI_SCALE>(a, s);
   if (!trans && sym && epi == EPI_SCALE && to == DT_F16) return go<T, f16, true, EPI_SCALE>(a, s);
   if (!trans && sym && epi == EPI_POLY && to == DT_BF16) return go<T, bf16, true, EPI_POLY>(a, s);
-  if (!trans && !sym && epi == EPI_AXPY && to == DT_BF16) return go<T, bf16, false, EPI_AXPY>(a, s);
+  if (!trans && !sym && epi == EPI_SCALE && to == DT_BF16) return go<T, bf16, false, EPI_SCALE>(a, s);
   if (!trans && !sym && epi == EPI_FINAL && to == DT_BF16) return go<T, bf16, false, EPI_FINAL>(a, s);
   if (!trans && !sym && epi == EPI_FINAL && to == DT_F32) return go<T, float, false, EPI_FINAL>(a, s);
   // K-major operands (A = Y^T Y from the transposed copy)

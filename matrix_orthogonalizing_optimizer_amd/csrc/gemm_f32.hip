@@ -15,7 +15,7 @@ template <int T>
 hipError_t dispatch(int to, bool sym, int epi, bool trans, const GemmArgs& a, hipStream_t s) {
   if (!trans && sym && epi == EPI_SCALE && to == DT_F32) return go<T, float, true, EPI_SCALE>(a, s);
   if (!trans && sym && epi == EPI_POLY && to == DT_F32) return go<T, float, true, EPI_POLY>(a, s);
-  if (!trans && !sym && epi == EPI_AXPY && to == DT_F32) return go<T, float, false, EPI_AXPY>(a, s);
+  if (!trans && !sym && epi == EPI_SCALE && to == DT_F32) return go<T, float, false, EPI_SCALE>(a, s);
   if (!trans && !sym && epi == EPI_FINAL && to == DT_F32) return go<T, float, false, EPI_FINAL>(a, s);
   if (!trans && !sym && epi == EPI_FINAL && to == DT_BF16) return go<T, bf16, false, EPI_FINAL>(a, s);
   if (trans && sym && epi == EPI_SCALE && to == DT_F32) return go<T, float, true, EPI_SCALE, true>(a, s);

@@ -5,14 +5,16 @@
 
 namespace muon {
 
-enum : int32_t { EPI_SCALE = 0, EPI_POLY = 1, EPI_AXPY = 2, EPI_FINAL = 3 };
+// Epilogues: C = alpha L R^T (SCALE); C = alpha L R^T + beta E + gamma I
+// (POLY); the fused parameter update (FINAL).
+enum : int32_t { EPI_SCALE = 0, EPI_POLY = 1, EPI_FINAL = 2 };
 enum : int32_t { SEL_ONE = 0, SEL_INV_S = 1, SEL_INV_S2 = 2 };
 enum : int32_t { FINAL_UPDATE = 0, FINAL_STORE = 1 };
 
 struct GemmArgs {
   const void* L;   // M x K, K contiguous
   const void* R;   // N x K, K contiguous
-  const void* E;   // epilogue addend (EPI_POLY, EPI_AXPY), same layout as C
+  const void* E;   // epilogue addend (EPI_POLY), same layout as C
   void* C;         // direct output (M x N), or null; EPI_FINAL writes the parameters (TO = their dtype)
   void* C2;        // mirror output (N x M, the transpose), or null; C for a symmetric product
   int64_t ldl, ldr, lde, ldc, ldc2;
