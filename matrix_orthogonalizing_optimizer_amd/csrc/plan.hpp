@@ -59,7 +59,10 @@ muon_status build_plan(const muon_param_shape* table, int32_t n, const muon_plan
                        PlanImpl& out);
 
 constexpr size_t WS_ALIGN = 256;
-constexpr size_t CHUNK_CAP_BYTES = size_t(8) << 30;  // data bytes per chunk
+// data bytes per chunk: large enough that a bucket of Llama-3-8B-sized
+// units runs as one chunk (fewer launches, and the symmetric products' last
+// partial round of 256 tiles is paid once per bucket)
+constexpr size_t CHUNK_CAP_BYTES = size_t(24) << 30;
 constexpr int32_t MAX_NS_STEPS = 64;
 
 }  // namespace muon
