@@ -1,17 +1,17 @@
 // Grouped MFMA GEMM for the Newton-Schulz contractions on gfx950.
 //
 // One launch computes, for every unit u of a bucket chunk,
-//     C_u = epilogue( L_u . R_u^T )
-// with L_u (M x K) and R_u (N x K) both row-major with K contiguous.  The
-// Newton-Schulz step of "Muon Optimizer and the Distributed Implementation"
-// (section "Newton-Schulz Iteration"),
-//     A = X X^T,   B = b A + c A A,   X' = a X + B X = P X  (P = a I + B),
-// is run with every unit kept in both orientations, X (m x n) and Y = X^T
-// (n x m): A = X X^T and B = c A A^T + b A are symmetric products (only
+//     C_u = epilogue( L_u . R_u^T )      (TRANS = false: L_u (M x K) and
+//                                         R_u (N x K) row-major, K contiguous)
+//     C_u = epilogue( L_u^T . R_u )      (TRANS = true: L_u (K x M) and
+//                                         R_u (K x N) row-major, K-major)
+// The Newton-Schulz step of "Muon Optimizer and the Distributed
+// Implementation" (section "Newton-Schulz Iteration"),
+//     A = X X^T,   X' = a X + (b A + c A A) X = P X,   P = a I + b A + c A A,
+// runs on the transposed copy Y = X^T (n x m) only: A = Y^T Y is a symmetric
+// K-major product, P = c A A^T + b A + a I a symmetric row-major one (only
 // upper-triangle tiles are computed, then mirrored), and the update is
-// computed transposed, Y' = Y P^T (P is symmetric), its epilogue
-// storing Y' directly and X' = Y'^T through the mirror pass.  So both
-// operands of every product are K-contiguous.
+// computed transposed, Y' = Y P^T (P is symmetric).
 //
 // Tiling (CDNA4, wave64): a 256-thread workgroup owns a BM x BN output tile
 // (256 x 256, or 128 x 128 for small m); 2 x 2 waves each own (BM/2) x (BN/2)
@@ -25,7 +25,9 @@
 // lane, 8 rows x 128 bytes per instruction), two stages in an LDS ring, so no
 // registers hold staged data.  The 16-byte chunks of a row are XOR-swizzled
 // with (row & 7) ^ ((row >> 3) & 1), which keeps the 32-row fragment reads
-// free of bank conflicts for 8 and for 16 lanes per LDS cycle.  Out-of-range
+// free of bank conflicts for 8 and for 16 lanes per LDS cycle.  A K-major
+// stage holds 64 K-rows of BM elements per operand, and fragments come out
+// of it through ds_read_b64_tr_b16 (4 x 16 blocks read transposed).  Out-of-range
 // rows and K chunks get an out-of-range buffer offset and read as zero; along
 // K a 16-byte chunk is read when its first element is in range, which relies
 // on leading dimensions that are multiples of 8 with zero padding (the
@@ -42,10 +44,11 @@
 // between two MFMAs.
 //
 // Epilogue: each wave stages its accumulators in LDS one 32-row strip at a
-// time, turns them into output values in place (scale, polynomial, axpy with
-// the addend E read as 16-byte rows), then stores the strip with 16-byte row
-// chunks (direct pass, to C) and/or transposed (mirror pass, to C2: the
-// symmetric mirror, X' of the update, or the transposed parameter block).
+// time, reads the strip back as 16-byte row pieces, turns them into output
+// values (scale; polynomial with the addend E read from global memory one
+// strip ahead; or the fused parameter update), and stores them as row chunks
+// (direct pass, to C) and/or transposed (mirror pass, to C2: the symmetric
+// mirror, or the transposed parameter block of a wide unit).
 #pragma once
 
 #include "kernel_args.hpp"
