@@ -581,32 +581,44 @@ void gemm_kernel(const GemmArgs a) {
   };
   if constexpr (EPI == EPI_POLY) load_e(0, pe[0]);
 
+  // EPI_FINAL: the old parameter values of strip i at the positions of the
+  // pass that writes them, loaded like E one strip ahead.  A per-strip buffer
+  // resource starts at the strip's first parameter row, so offsets stay
+  // small whatever the parameter's size; pieces not wholly inside the block
+  // stay zero here and take the element-wise path, which reads W itself.
+  Raw8<TO> pwb[2][NT];
+  auto load_w = [&](int i, Raw8<TO>(&dst)[NT]) {
+    const int gri = row0 + wm * (BM / 2) + i * 32;
+    const int prow0 = fdirect ? gri : gc0;  // first parameter row the strip writes
+    const int prow_lim = fdirect ? a.M : a.N, pcol_lim = fdirect ? a.N : a.M;
+    const int rows_in = max(0, min(fdirect ? 32 : WN, prow_lim - prow0));
+    const TO* base = reinterpret_cast<const TO*>(d.w) + (int64_t)min(prow0, prow_lim) * d.ld;
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(base, (uint32_t)((int64_t)rows_in * d.ld * (int64_t)sizeof(TO)));
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      int r, c;  // parameter row (from prow0) and first column of piece t
+      if (fdirect) {
+        r = dr0 + DRS * t;
+        c = gj;
+      } else {
+        int jj, c8;
+        mpos(t, jj, c8);
+        r = jj;
+        c = gri + c8;
+      }
+      const uint32_t off = wpre && c + 8 <= pcol_lim ? (uint32_t)(((int64_t)r * d.ld + c) * (int64_t)sizeof(TO)) : OOB;
+#pragma unroll
+      for (int h = 0; h < (int)(sizeof(TO) / 2); ++h)
+        dst[t].w[h] = __builtin_amdgcn_raw_buffer_load_b128(wrs, off + 16 * h, 0, 0);
+    }
+  };
+  if constexpr (EPI == EPI_FINAL) load_w(0, pwb[0]);
+
 #pragma unroll
   for (int i = 0; i < WTM; ++i) {
     const int gr0 = row0 + wm * (BM / 2) + i * 32;  // global row of strip row 0
 
-    // the fused update's old parameter values (positions of the pass that
-    // writes them) go out before this strip's LDS work
-    Raw8<TO> pw[NT];
-    if constexpr (EPI == EPI_FINAL) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        raw_zero(pw[t]);
-        int pr, pc;  // parameter row, first column
-        if (fdirect) {
-          pr = gr0 + dr0 + DRS * t;
-          pc = gj;
-        } else {
-          int jj, c8;
-          mpos(t, jj, c8);
-          pr = gc0 + jj;
-          pc = gr0 + c8;
-        }
-        const int prow_lim = fdirect ? a.M : a.N, pcol_lim = fdirect ? a.N : a.M;
-        if (wpre && pr < prow_lim && pc + 8 <= pcol_lim)
-          raw_load8(reinterpret_cast<const TO*>(d.w) + (int64_t)pr * d.ld + pc, pw[t]);
-      }
-    }
+    Raw8<TO>(&pw)[NT] = pwb[i & 1];
 
     // accumulators of MFMA row-tile i -> strip[32][WN]
 #pragma unroll
@@ -640,6 +652,9 @@ void gemm_kernel(const GemmArgs a) {
       const f32x4 hi = *reinterpret_cast<const f32x4*>(sp + 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) { v[t][e] = lo[e]; v[t][e + 4] = hi[e]; }
+    }
+    if constexpr (EPI == EPI_FINAL) {
+      if (i + 1 < WTM) load_w(i + 1, pwb[(i + 1) & 1]);
     }
     if constexpr (EPI == EPI_POLY) {
       if (i + 1 < WTM) load_e(i + 1, pe[(i + 1) & 1]);
