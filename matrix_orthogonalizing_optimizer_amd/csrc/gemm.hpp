@@ -51,6 +51,8 @@
 // mirror, or the transposed parameter block of a wide unit).
 #pragma once
 
+#include <type_traits>
+
 #include "kernel_args.hpp"
 
 namespace muon {
@@ -266,6 +268,14 @@ template <int ROWB> __device__ __forceinline__ uint2 lds_read_tr16_step(uint32_t
     case 5: return lds_read_tr16_off<36 * ROWB>(addr);
     case 6: return lds_read_tr16_off<48 * ROWB>(addr);
     default: return lds_read_tr16_off<52 * ROWB>(addr);
+  }
+}
+
+// f(integral_constant<int, B>), ..., f(integral_constant<int, E - 1>), in order.
+template <int B, int E, typename F> __device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
   }
 }
 
@@ -614,8 +624,11 @@ void gemm_kernel(const GemmArgs a) {
   };
   if constexpr (EPI == EPI_FINAL) load_w(0, pwb[0]);
 
-#pragma unroll
-  for (int i = 0; i < WTM; ++i) {
+  // one pass per MFMA row-tile i, with i a compile-time constant (a large
+  // body can exceed the unroller's budget, and a run-time i would send the
+  // accumulators to scratch memory)
+  static_for<0, WTM>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
     const int gr0 = row0 + wm * (BM / 2) + i * 32;  // global row of strip row 0
 
     Raw8<TO>(&pw)[NT] = pwb[i & 1];
@@ -768,7 +781,7 @@ void gemm_kernel(const GemmArgs a) {
       }
     }
     __syncthreads();
-  }
+  });
 }
 
 }  // namespace muon
