@@ -41,6 +41,8 @@ def parse():
                    help="override the workload's Newton-Schulz method")
     p.add_argument("--cpu-sample", default=",".join(["1024x4096"] * 8),
                    help="unit shapes the oracle is timed on")
+    p.add_argument("--no-probes", action="store_true",
+                   help="skip the measured MFMA and copy ceilings")
     return p.parse_args()
 
 
@@ -108,6 +110,9 @@ def main():
 
     ns_flops = wl.hp["ns_steps"] * configs.ns_flops(table)
     tflops = ns_flops / (ms_per_step * 1e-3) / 1e12
+    exe = executed_flops(mo.muon_plan_buckets(plan), wl.hp["ns_steps"])
+    exe_total = sum(exe.values())
+    probes = None if args.no_probes else measure_probes(mo, torch, stream)
 
     kernels = {}
     for name, r in kt.items():
@@ -116,6 +121,8 @@ def main():
              "avg_launch_ms": avg}
         if r["flops"] > 0:
             e["tflops"] = r["flops"] / (r["total_ms"] * 1e-3) / 1e12
+        if name in exe:
+            e["executed_tflops"] = exe[name] * args.steps / (r["total_ms"] * 1e-3) / 1e12
         if r["bytes"] > 0:
             e["gbs"] = r["bytes"] / (r["total_ms"] * 1e-3) / 1e9
         kernels[name] = e
@@ -126,6 +133,8 @@ def main():
                 "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
                 "flops_per_launch": d["flops"] / d["launches"],
                 "avg_launch_ms": d["total_ms"] / d["launches"], "traffic": None}
+    if probes:
+        roofline["frac_of_probed_peak"] = achieved / probes["mfma_bf16_tflops"]
     if dom == "ns_update_PX" and wl.method == "standard":
         # algorithmic HBM bytes of the update GEMM Y' = Y P^T: read Y (n x m)
         # and P (m x m), write Y'
@@ -155,15 +164,80 @@ def main():
         "dtype": "bf16" if table[0][1] == 1 else "f32",
         "data": "synthetic",
         "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
+        "executed_tflops": exe_total / (ms_per_step * 1e-3) / 1e12,
+        "executed_pct_bf16_peak": 100.0 * exe_total / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "probed_peaks": probes,
         "config": {"workload": wl.name, "units": n_units, "buckets": len(mo.muon_plan_buckets(plan)),
                    "ns_steps": wl.hp["ns_steps"], "ns_method": wl.method,
                    "muon_elements": muon_elems, "adamw_elements": adam_elems,
-                   "ns_nominal_tflop_per_step": ns_flops / 1e12},
+                   "ns_nominal_tflop_per_step": ns_flops / 1e12,
+                   "ns_executed_tflop_per_step": exe_total / 1e12},
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def executed_flops(buckets, steps):
+    """FLOPs the GEMM kernels execute in one step, per timing family: output
+    tiles computed x 2 T^2 K, T the tile side (256, or 128 when m <= 192).
+    Padded tiles count; symmetric products compute upper-triangle tiles only.
+    Bucket tuples: (m, n, tall, param dtype, compute dtype, method, first, count)."""
+    out = {}
+
+    def add(name, v):
+        out[name] = out.get(name, 0.0) + v
+
+    for m, n, _tall, _pdt, _cdt, method, _first, count in buckets:
+        T = 256 if m > 192 else 128
+        t, tn = -(-m // T), -(-n // T)
+        tri, sq, rect = t * (t + 1) // 2, t * t, tn * t
+        f = 2.0 * T * T * count
+        if method == 0:  # standard
+            add("ns_gram_A", steps * tri * f * n)
+            add("ns_poly_P", steps * tri * f * m)
+            if steps > 1:
+                add("ns_update_PX", (steps - 1) * rect * f * m)
+            add("ns_final_update", rect * f * m)
+        else:  # Gram
+            add("gram_r0", tri * f * n)
+            add("gram_p", steps * tri * f * m)
+            if steps > 1:
+                add("gram_q", (steps - 1) * sq * f * m)
+                add("gram_t", (steps - 1) * sq * f * m)
+                add("gram_r", (steps - 1) * tri * f * m)
+            add("ns_final_update", rect * f * m)
+    return out
+
+
+def measure_probes(mo, torch, stream):
+    """Ceilings measured in this process on this device, each timed with
+    events on the launch stream, best of three: the library's register-only
+    bf16 MFMA loop (two workgroups of 4 waves per compute unit) and its
+    streaming copy of 2 GiB (2 x 2 GiB through HBM)."""
+    sink = torch.empty(512, dtype=torch.float32, device="cuda:0")
+    src = torch.empty(1 << 31, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty(1 << 31, dtype=torch.uint8, device="cuda:0")
+
+    def best_of(fn, amount):
+        fn()  # warm
+        best = 0.0
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            best = max(best, amount / (e0.elapsed_time(e1) * 1e-3))
+        return best
+
+    flops = 512 * 4 * 1024 * 8 * 32768.0
+    mfma = best_of(lambda: mo.muon_probe_mfma(512, 1024, sink, stream=stream), flops) / 1e12
+    copy = best_of(lambda: mo.muon_probe_copy(src, dst, 1 << 31, stream=stream), 2.0 * (1 << 31)) / 1e9
+    del src, dst
+    return {"mfma_bf16_tflops": mfma, "mfma_frac_of_nominal": mfma / BF16_PEAK_TFLOPS,
+            "copy_gbs": copy, "copy_frac_of_nominal": copy / HBM_PEAK_GBS}
 
 
 def unit_shapes(table):

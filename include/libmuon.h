@@ -229,6 +229,24 @@ typedef struct {
 muon_status muon_timing_enable(int32_t enable);
 muon_status muon_timing_collect(muon_kernel_timing* out, int32_t cap, int32_t* n);
 
+/* Measurement aids for benchmarks; not part of the optimizer step.  Both
+ * only enqueue on stream (a hipStream_t, null = default stream) and return.
+ * muon_probe_mfma: the device's sustained bf16 matrix-core rate.  Launches
+ *   `workgroups` workgroups of 4 waves; each wave runs `iters` rounds of 8
+ *   independent v_mfma_f32_32x32x16_bf16 from registers, and each workgroup
+ *   writes one float to sink (device memory, `workgroups` floats, owned by
+ *   the caller).  *flops (host) receives the FLOPs of the launch
+ *   (workgroups * 4 * iters * 8 * 32768).  MUON_E_ARG if a count is not
+ *   positive or a pointer is null; MUON_E_HIP if the launch fails.
+ * muon_probe_copy: the device's streaming copy rate.  Copies `bytes` from
+ *   src to dst (device memory, non-overlapping, owned by the caller) with
+ *   16-byte non-temporal loads and stores, one contiguous 16 KiB block per
+ *   workgroup; 2 * bytes move through HBM.
+ *   MUON_E_ARG if bytes is 0 or not a multiple of 16, or a pointer is null
+ *   or not 16-byte aligned; MUON_E_HIP if the launch fails. */
+muon_status muon_probe_mfma(int32_t workgroups, int32_t iters, float* sink, double* flops, void* stream);
+muon_status muon_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+
 /* Newton-Schulz coefficient schedules: writes steps x 3 floats (a_k, b_k,
  * c_k) to out (capacity cap floats) for muon_hparams.coeffs.
  *   MUON_COEFF_QUINTIC  (3.4445, -4.7750, 2.0315) at every step ([Blog]

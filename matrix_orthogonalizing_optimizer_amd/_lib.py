@@ -27,7 +27,8 @@ MUON_COEFF_QUINTIC, MUON_COEFF_HYBRID = 0, 1
 EXPORTED = ["muon_plan_create", "muon_plan_destroy", "muon_plan_workspace_bytes",
             "muon_plan_buckets", "muon_plan_units", "muon_step", "ns_orthogonalize",
             "ns_orthogonalize_workspace_bytes", "muon_timing_enable", "muon_timing_collect",
-            "muon_ns_coefficients", "muon_status_string", "muon_version"]
+            "muon_ns_coefficients", "muon_status_string", "muon_version", "muon_probe_mfma",
+            "muon_probe_copy"]
 
 
 class MuonError(RuntimeError):
@@ -102,6 +103,10 @@ def lib():
     L.muon_timing_enable.restype = i32
     L.muon_timing_collect.argtypes = [ctypes.POINTER(MuonKernelTiming), i32, ctypes.POINTER(i32)]
     L.muon_timing_collect.restype = i32
+    L.muon_probe_mfma.argtypes = [i32, i32, vp, ctypes.POINTER(ctypes.c_double), vp]
+    L.muon_probe_mfma.restype = i32
+    L.muon_probe_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+    L.muon_probe_copy.restype = i32
     L.muon_ns_coefficients.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_float), sz]
     L.muon_ns_coefficients.restype = i32
     L.muon_status_string.argtypes = [i32]
@@ -276,6 +281,25 @@ def muon_timing_collect() -> dict:
     return {arr[i].name.decode(): {"launches": arr[i].launches, "total_ms": arr[i].total_ms,
                                    "flops": arr[i].flops, "bytes": arr[i].bytes}
             for i in range(min(n.value, cap))}
+
+
+def muon_probe_mfma(workgroups: int, iters: int, sink, stream=None) -> float:
+    """Enqueue the register-only bf16 MFMA loop; returns its FLOPs.  sink:
+    device tensor of at least `workgroups` float32."""
+    if hasattr(sink, "numel") and sink.numel() < workgroups:
+        raise ValueError("sink holds fewer than `workgroups` floats")
+    flops = ctypes.c_double()
+    _check("muon_probe_mfma", lib().muon_probe_mfma(workgroups, iters, _ptr(sink), ctypes.byref(flops),
+                                                     _stream(stream)))
+    return flops.value
+
+
+def muon_probe_copy(src, dst, nbytes: int, stream=None) -> None:
+    """Enqueue the streaming copy of nbytes from src to dst (device tensors)."""
+    for t in (src, dst):
+        if hasattr(t, "numel") and t.numel() * t.element_size() < nbytes:
+            raise ValueError("buffer smaller than nbytes")
+    _check("muon_probe_copy", lib().muon_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
 
 
 def muon_status_string(status: int) -> str:

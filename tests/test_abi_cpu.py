@@ -175,3 +175,18 @@ def test_ns_orthogonalize_validation():
     assert f(None, 64, 96, 96, 1, 5, None, 0, 0x10000, nb, None) == -1
     assert f(0x1000, 64, 96, 96, 1, 5, None, 0, 0x10000, nb - 1, None) == -5
     assert f(0x1000, 0, 96, 96, 1, 5, None, 0, None, 0, None) == 0   # empty: nothing to do
+
+
+def test_probe_validation():
+    L = _lib_or_skip()
+    import ctypes as C
+    fl = C.c_double()
+    assert L.muon_probe_mfma(0, 10, 0x1000, C.byref(fl), None) == -1
+    assert L.muon_probe_mfma(4, 0, 0x1000, C.byref(fl), None) == -1
+    assert L.muon_probe_mfma(4, 10, None, C.byref(fl), None) == -1
+    assert L.muon_probe_mfma(4, 10, 0x1000, None, None) == -1
+    assert L.muon_probe_copy(0x1000, 0x2000, 0, None) == -1      # nothing to copy
+    assert L.muon_probe_copy(0x1000, 0x2000, 24, None) == -1     # not a multiple of 16
+    assert L.muon_probe_copy(0x1008, 0x2000, 32, None) == -1     # misaligned source
+    assert L.muon_probe_copy(0x1000, 0x2004, 32, None) == -1     # misaligned destination
+    assert L.muon_probe_copy(None, 0x2000, 32, None) == -1
