@@ -43,6 +43,9 @@ def parse():
                    help="unit shapes the oracle is timed on")
     p.add_argument("--no-probes", action="store_true",
                    help="skip the measured MFMA and copy ceilings")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run the library's streaming copy of 1 GiB three times and exit: the "
+                        "reference dispatch that scales the FETCH_SIZE / WRITE_SIZE counters")
     return p.parse_args()
 
 
@@ -59,6 +62,16 @@ def main():
 
     mo.lib()
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        for _ in range(3):
+            mo.muon_probe_copy(src, dst, nbytes)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_per_dispatch": nbytes, "dispatches": 3,
+                                               "kernel": "probe_copy_kernel"}}))
+        return
     wl = configs.ALL[args.workload]()
     if args.ns_method:
         wl.method = args.ns_method
