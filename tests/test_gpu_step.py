@@ -243,3 +243,28 @@ def test_auto_method_mixed_plan():
         assert rel(f64(outs[i]), ref["O"][i]) <= 2e-2, (i, rel(f64(outs[i]), ref["O"][i]))
         dw_ref = stored(ref["W"][i], torch.bfloat16) - W0[i]
         assert rel(f64(P[i]) - W0[i], dw_ref) <= 2e-2
+
+
+def test_empty_parameters_in_the_table():
+    """Empty Muon and AdamW parameters (null data pointers) are skipped: the
+    other parameters come out bit-identical to a table without them."""
+    print("muon_step with empty parameters", flush=True)
+    d = dev()
+    full = [(0, 1, 0, 96, 0, 0), (0, 1, 256, 384, 0, 0), (1, 1, 1, 0, 0, 0), (1, 1, 1, 256, 0, 0)]
+    kept = [full[1], full[3]]
+    wl = configs.Workload("e", kept, ["w", "b"], rank=4, hp=configs._hp())
+    P, M, EA, ES = _state(wl, d)
+    G = [g.to(d) for g in gen.make_grads(wl, 0, "cpu")]
+    Pa, Ma = [p.clone() for p in P], [m.clone() if m is not None else None for m in M]
+    EAa, ESa = [x.clone() if x is not None else None for x in EA], [x.clone() if x is not None else None for x in ES]
+    StepRunner(kept, device=d).step(P, G, M, EA, ES, hp_from(wl.hp))
+    e16 = lambda r, c: torch.empty(r, c, dtype=torch.bfloat16, device=d)
+    e32 = lambda r, c: torch.empty(r, c, dtype=torch.float32, device=d)
+    StepRunner(full, device=d).step([e16(0, 96), Pa[0], e16(1, 0), Pa[1]],
+                                    [e16(0, 96), G[0], e16(1, 0), G[1]],
+                                    [e32(0, 96), Ma[0], None, None],
+                                    [None, None, e32(1, 0), EAa[1]], [None, None, e32(1, 0), ESa[1]],
+                                    hp_from(wl.hp))
+    torch.cuda.synchronize()
+    assert torch.equal(Pa[0], P[0]) and torch.equal(Pa[1], P[1])
+    assert torch.equal(Ma[0], M[0]) and torch.equal(EAa[1], EA[1]) and torch.equal(ESa[1], ES[1])
