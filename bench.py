@@ -205,7 +205,7 @@ def executed_flops(buckets, steps):
     for m, n, _tall, _pdt, _cdt, method, _first, count in buckets:
         T = 256 if m > 192 else 128
         t, tn = -(-m // T), -(-n // T)
-        tri, sq, rect = t * (t + 1) // 2, t * t, tn * t
+        tri, rect = t * (t + 1) // 2, tn * t
         f = 2.0 * T * T * count
         if method == 0:  # standard
             add("ns_gram_A", steps * tri * f * n)
@@ -217,8 +217,8 @@ def executed_flops(buckets, steps):
             add("gram_r0", tri * f * n)
             add("gram_p", steps * tri * f * m)
             if steps > 1:
-                add("gram_q", (steps - 1) * sq * f * m)
-                add("gram_t", (steps - 1) * sq * f * m)
+                add("gram_q", (steps - 1) * tri * f * m)
+                add("gram_t", (steps - 1) * tri * f * m)
                 add("gram_r", (steps - 1) * tri * f * m)
             add("ns_final_update", rect * f * m)
     return out

@@ -17,6 +17,8 @@
 // Gram method (DeepSpeed page: iterate on the square Gram matrix R = X X^T):
 //   R = 2^e X0 X0^T / s^2 (power-of-two scaled, fp16 for a bf16 bucket);
 //   P_k = a I + b R + c R^2;  Q <- P_k Q;  R <- P_k R P_k;  O = Q X0 / s.
+//   All of R_k, P_k, Q are polynomials in R_0: symmetric and commuting, so
+//   every m x m product is computed as a symmetric one (upper tiles).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -212,29 +214,20 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
     } else {
       int zn = 0;
       while (zn == z || zn == p) ++zn;
-      // Z' = Z P; the last one is stored transposed, as Q
-      g = gemm_args(T, cnt, (int)m, (int)m, (int)m, false);
-      g.L = PZ[z]; g.ldl = b.mp; g.sL = ss;
-      g.R = PZ[p]; g.ldr = b.mp; g.sR = ss;
-      g.beta = 0.f;
-      if (last) {
-        g.C2 = PZ[zn]; g.ldc2 = b.mp; g.sC2 = ss;
-      } else {
-        g.C = PZ[zn]; g.ldc = b.mp; g.sC = ss;
-      }
+      // Z' = Z P.  Every R_k, P_k and their products are polynomials in R_0,
+      // so they commute and are symmetric: Z = Q, and Z P is computed as a
+      // symmetric product (upper tiles + mirror); the last one is Q itself
+      g = sym_args(PZ[z], b.mp, ss, PZ[p], b.mp, ss, (int)m, PZ[zn]);
       HIP_TRY(timed(F_GRAM_Q, mmm, 0.0, st,
-                    [&] { return launch_gemm(T, sdt, last ? qdt_last : sdt, false, EPI_SCALE, false, g, st); }));
+                    [&] { return launch_gemm(T, sdt, last ? qdt_last : sdt, true, EPI_SCALE, false, g, st); }));
       z = zn;
     }
     if (!last) {
-      // Tm = P R  (R symmetric: its rows serve as R^T)
-      g = gemm_args(T, cnt, (int)m, (int)m, (int)m, false);
-      g.L = PZ[p]; g.ldl = b.mp; g.sL = ss;
-      g.R = R; g.ldr = b.mp; g.sR = ss;
-      g.C = Tm; g.ldc = b.mp; g.sC = ss;
-      g.beta = 0.f;
+      // Tm = P R  (R symmetric: its rows serve as R^T; P and R commute, so
+      // Tm is symmetric too: upper tiles + mirror)
+      g = sym_args(PZ[p], b.mp, ss, R, b.mp, ss, (int)m, Tm);
       HIP_TRY(timed(F_GRAM_T, mmm, 0.0, st,
-                    [&] { return launch_gemm(T, sdt, sdt, false, EPI_SCALE, false, g, st); }));
+                    [&] { return launch_gemm(T, sdt, sdt, true, EPI_SCALE, false, g, st); }));
       // R = Tm P  (P symmetric; the result is symmetric: upper tiles + mirror)
       g = sym_args(Tm, b.mp, ss, PZ[p], b.mp, ss, (int)m, R);
       HIP_TRY(timed(F_GRAM_R, mmm, 0.0, st,

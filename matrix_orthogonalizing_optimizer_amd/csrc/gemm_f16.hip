@@ -14,6 +14,7 @@ hipError_t go(const GemmArgs& a, hipStream_t s) {
 template <int T>
 hipError_t dispatch(int to, bool sym, int epi, bool trans, const GemmArgs& a, hipStream_t s) {
   if (!trans && sym && epi == EPI_SCALE && to == DT_F16) return go<T, f16, true, EPI_SCALE>(a, s);
+  if (!trans && sym && epi == EPI_SCALE && to == DT_BF16) return go<T, bf16, true, EPI_SCALE>(a, s);
   if (!trans && sym && epi == EPI_POLY && to == DT_F16) return go<T, f16, true, EPI_POLY>(a, s);
   if (!trans && sym && epi == EPI_POLY && to == DT_BF16) return go<T, bf16, true, EPI_POLY>(a, s);
   if (!trans && !sym && epi == EPI_SCALE && to == DT_F16) return go<T, f16, false, EPI_SCALE>(a, s);
