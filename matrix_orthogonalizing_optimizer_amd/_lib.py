@@ -218,12 +218,41 @@ def make_hparams(lr=0.02, momentum=0.95, weight_decay=0.1, nesterov=True, ns_ste
     return hp
 
 
+def _check_buffer(name, t, rows, cols, dtype):
+    """A torch tensor handed to muon_step must be the contiguous rows x cols
+    buffer of the table's dtype: the library addresses it from its pointer
+    and the table alone.  Raw integer pointers and None pass unchecked (the
+    library rejects a null pointer where one is required)."""
+    if t is None or isinstance(t, int) or not hasattr(t, "data_ptr"):
+        return
+    import torch
+    want = torch.float32 if dtype == MUON_F32 else torch.bfloat16
+    if t.dtype != want:
+        raise ValueError(f"{name}: dtype {t.dtype}, the table says {want}")
+    if t.numel() != rows * cols or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous {rows} x {cols} tensor, got {tuple(t.shape)}")
+
+
 def muon_step(plan: Plan, params, grads, moms, exp_avgs, exp_avg_sqs, hp: MuonHparams, workspace,
               stream=None, update_outs=None) -> None:
     """One optimizer step; lists follow the plan's table order (None where a
     buffer does not apply).  workspace: a device tensor (or pointer) of at
     least muon_plan_workspace_bytes(plan) bytes."""
     n = len(plan.table)
+    for name, lst in (("params", params), ("grads", grads), ("moms", moms), ("exp_avgs", exp_avgs),
+                      ("exp_avg_sqs", exp_avg_sqs), ("update_outs", update_outs)):
+        if lst is not None and len(lst) != n:
+            raise ValueError(f"{name}: {len(lst)} entries for a table of {n}")
+    for i, (kind, dt, rows, cols, _split, _sd) in enumerate(plan.table):
+        _check_buffer(f"params[{i}]", params[i], rows, cols, dt)
+        _check_buffer(f"grads[{i}]", grads[i], rows, cols, dt)
+        if kind == MUON_KIND_MUON:
+            _check_buffer(f"moms[{i}]", moms[i], rows, cols, MUON_F32)
+            if update_outs is not None:
+                _check_buffer(f"update_outs[{i}]", update_outs[i], rows, cols, MUON_F32)
+        else:
+            _check_buffer(f"exp_avgs[{i}]", exp_avgs[i], rows, cols, MUON_F32)
+            _check_buffer(f"exp_avg_sqs[{i}]", exp_avg_sqs[i], rows, cols, MUON_F32)
     arr = (MuonParamPtrs * max(n, 1))()
     for i in range(n):
         arr[i] = MuonParamPtrs(_ptr(params[i]), _ptr(grads[i]), _ptr(moms[i]), _ptr(exp_avgs[i]),

@@ -190,3 +190,26 @@ def test_probe_validation():
     assert L.muon_probe_copy(0x1008, 0x2000, 32, None) == -1     # misaligned source
     assert L.muon_probe_copy(0x1000, 0x2004, 32, None) == -1     # misaligned destination
     assert L.muon_probe_copy(None, 0x2000, 32, None) == -1
+
+
+def test_step_binding_checks_buffers():
+    """The Python binding refuses tensors that do not match the table (no
+    launch happens: the check precedes the library call)."""
+    _lib_or_skip()
+    import torch
+    plan = mo.muon_plan_create([(0, 1, 4, 8, 0, 0), (1, 0, 1, 8, 0, 0)])
+    hp = mo.make_hparams()
+    ok = [torch.zeros(4, 8, dtype=torch.bfloat16), torch.zeros(1, 8, dtype=torch.float32)]
+    moms = [torch.zeros(4, 8), None]
+    ea = [None, torch.zeros(1, 8)]
+    es = [None, torch.zeros(1, 8)]
+    bad_cases = [
+        ([torch.zeros(4, 8, dtype=torch.float32), ok[1]], ok, moms),          # param dtype
+        ([torch.zeros(4, 9, dtype=torch.bfloat16), ok[1]], ok, moms),         # param shape
+        (ok, [torch.zeros(8, 4, dtype=torch.bfloat16).t(), ok[1]], moms),     # not contiguous
+        (ok, ok, [torch.zeros(4, 8, dtype=torch.bfloat16), None]),            # momentum dtype
+        (ok[:1], ok, moms),                                                   # list length
+    ]
+    for p, g, m in bad_cases:
+        with pytest.raises(ValueError):
+            mo.muon_step(plan, p, g, m, ea, es, hp, 0x10000)
