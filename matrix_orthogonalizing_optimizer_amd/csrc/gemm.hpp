@@ -115,6 +115,14 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, void* ds
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)dst, 16, off, 0, 0, 0);
 }
 
+// A wave-uniform pointer moved to scalar registers.
+template <typename P> __device__ __forceinline__ P uniform_ptr(P p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (P)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Upper-triangle tile t (row-major over bi <= bj) of a T x T tile grid.
 __device__ __forceinline__ void upper_tile(int t, int T, int& bi, int& bj) {
   int i = 0;
@@ -544,7 +552,16 @@ void gemm_kernel(const GemmArgs a) {
   float keep = 1.f, step = 0.f;
   UnitDesc d;
   if constexpr (EPI == EPI_FINAL) {
+    // the descriptor arrives through a vector load (this kernel stores to
+    // global memory, so the compiler cannot prove a scalar load safe); its
+    // fields are uniform: move them to scalar registers, or every buffer
+    // resource built from them counts as divergent and each load of the old
+    // parameter values runs in a waterfall loop
     d = a.desc[unit];
+    d.w = uniform_ptr(d.w);
+    d.o = uniform_ptr(d.o);
+    d.ld = (int64_t)uniform_ptr((void*)(uintptr_t)d.ld);
+    d.scale = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, d.scale)));
     keep = 1.f - a.lr * a.wd;
     step = a.lr * d.scale;
   }

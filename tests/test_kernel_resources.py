@@ -4,9 +4,11 @@ cross-compiles for gfx950).
 - No kernel uses scratch memory: a spill or a stack array in these kernels
   (for example the GEMM accumulators indexed with a run-time value) costs a
   large part of their time, and nothing else would reveal it.
-- No direct-to-LDS operand copy of the GEMM sits in a waterfall loop: the
-  copies take a scalar buffer resource, and if the compiler cannot prove its
-  operands uniform it loops over the distinct values lane by lane.
+- No buffer load or store of the GEMM (direct-to-LDS operand copies, the
+  epilogue's loads of the addend and of the old parameter values, its
+  stores) sits in a waterfall loop: they take a scalar buffer resource, and
+  if the compiler cannot prove its operands uniform it loops over the
+  distinct values lane by lane.
 """
 import os
 import re
@@ -57,13 +59,15 @@ def test_no_scratch(resource_reports, src):
 
 
 @pytest.mark.parametrize("src", ["gemm_bf16.hip", "gemm_f16.hip", "gemm_f32.hip"])
-def test_operand_copies_not_in_waterfall_loops(tmp_path, src):
+def test_buffer_accesses_not_in_waterfall_loops(tmp_path, src):
     out = tmp_path / (src + ".s")
     _compile(src, ["-S", "-o", str(out)])
     lines = [l.strip() for l in out.read_text().splitlines()]
     copies = [i for i, l in enumerate(lines) if l.startswith("buffer_load_dword") and l.endswith(" lds")]
     assert copies, "no direct-to-LDS copies found"
-    for i in copies:
+    accesses = [i for i, l in enumerate(lines) if l.startswith(("buffer_load_dword", "buffer_store_dword"))]
+    assert len(accesses) > len(copies), "no epilogue buffer accesses found"
+    for i in accesses:
         window = lines[max(0, i - 4):i]
         assert not any(w.startswith("s_and_saveexec") for w in window), \
-            f"{src}: copy at line {i} is inside a waterfall loop: {window + [lines[i]]}"
+            f"{src}: buffer access at line {i} is inside a waterfall loop: {window + [lines[i]]}"
