@@ -39,9 +39,8 @@
 // barrier (after this wave's copies of the next stage landed and its reads
 // of this stage completed) frees this stage's slot; the last step's MFMAs
 // carry copies of the stage after next into it (all of them for K-major
-// operands; half for row-major ones, whose other half ride on the first two
-// steps of the next stage) and the fragment reads of the next stage's first
-// step.  A wave issues in order and an MFMA keeps the matrix pipe busy for
+// operands; half for row-major ones, whose other half ride on the first step
+// of the next stage) and the fragment reads of the next stage's first step.  A wave issues in order and an MFMA keeps the matrix pipe busy for
 // 32 cycles, so each memory instruction is placed between two MFMAs.
 //
 // Epilogue: each wave stages its accumulators in LDS one 32-row strip at a
@@ -328,14 +327,15 @@ void gemm_kernel(const GemmArgs a) {
   // XCD c & 7: at any time the 8 XCDs work on neighbouring chunks (mostly one
   // unit, whose operands then stay in the Infinity Cache), and the ~32 tiles an
   // XCD runs at once lie in one chunk (operand bands shared through its L2).
-  // S: 32 upper-triangle tiles, or two 4-row groups of a non-symmetric
-  // product (measured best of 16..272).  The tail short of a full round of 8
+  // S: 32 upper-triangle tiles (64 for the polynomial product), or two 4-row
+  // groups of a non-symmetric product (measured best of 16..272, re-checked
+  // against 16/64 and 4/16 groups after the copy schedule changed).  The tail short of a full round of 8
   // chunks is split into 8 contiguous ranges, so the map stays a bijection.
   int logical;
   {
     const int b = blockIdx.x, tot = a.totalTiles;
     const int xcd = b & 7, loc = b >> 3;
-    const int S = SYM ? 32 : 8 * a.tilesN;
+    const int S = SYM ? (EPI == EPI_POLY ? 64 : 32) : 8 * a.tilesN;
     const int full = tot / (8 * S);
     if (loc < full * S) {
       logical = (loc / S) * 8 * S + xcd * S + loc % S;
@@ -489,17 +489,17 @@ void gemm_kernel(const GemmArgs a) {
   // Row-major 256 x 256 products split the copies of a stage: half go out
   // during the last step of the stage two before it (right after the barrier
   // that frees its slot), one every other MFMA; the other half during the
-  // first two steps of the next stage, one every other MFMA of each step's
-  // second half (its first half carries the fragment reads).  All of them
-  // land before the barrier that precedes that stage's last step.  Issuing
-  // all 16 copies back to back in one step (one per MFMA) measured 4% slower
-  // on the update; the K-major product keeps that schedule, which measured
-  // 4% faster for it than the split one.
+  // first step of the next stage, one per MFMA of its second half (the first
+  // half carries the fragment reads).  All of them land before the barrier
+  // that precedes that stage's last step.  Issuing all 16 copies back to
+  // back in one step (one per MFMA) measured 4-5% slower on the update
+  // (spreading the second half over two steps: 0.5% slower than this); the
+  // K-major product keeps that schedule, which measured 1-4% faster for it
+  // than the split ones.
   constexpr bool SPLIT = !TRANS && NPAIR - NDR >= 8 && NQ == 16;
   constexpr int NQ3 = SPLIT ? NQ / 2 : NQ;
   constexpr int NQR = NQ - NQ3;
-  constexpr int RPS = (NPAIR - NDR) / 2;  // remainder copies per step
-  static_assert(!SPLIT || (NQ3 * 2 <= NPAIR && NQR <= RPS * (NSTEP - 1)), "split copy slots");
+  static_assert(!SPLIT || (NQ3 * 2 <= NPAIR && NQR <= NPAIR - NDR), "split copy slots");
 
   const int nk = (a.K + BK - 1) / BK;
   // prologue: stage 0 and the first part of stage 1 in flight, then stage 0 visible
@@ -527,8 +527,8 @@ void gemm_kernel(const GemmArgs a) {
         mfma_pair(p, s & 1);
         if (p < NDR) read_one(p, kt, s + 1, (s + 1) & 1);
         if constexpr (SPLIT) {
-          const int qq = s * RPS + (p - NDR) / 2;
-          if (p >= NDR && ((p - NDR) & 1) == 0 && qq < NQR) copy_one(NQ3 + qq, kt + 1);
+          const int qq = s * (NPAIR - NDR) + (p - NDR);
+          if (p >= NDR && qq < NQR) copy_one(NQ3 + qq, kt + 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
