@@ -121,13 +121,29 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
   HIP_TRY(timed(F_NORM, 0.0, 0.0, st, [&] { return launch_norm_finalize(d_part, b.km_tiles, d_aux, cnt, st); }));
 
   const int T = b.tile;
-  auto final_args = [&](GemmArgs& g) {
+  // The last product, fused with the parameter update, computed in the
+  // parameter block's own layout so that the epilogue writes whole rows: a
+  // tall unit's block has Y's layout, O^T = Y P^T (L = Y, R = P); a wide
+  // unit's has X's, O = P X = P Y^T (L = P, R = Y).  Yop: the n x m operand
+  // (Y), Pop: the m x m one (P, or Q for the Gram chain).
+  auto final_gemm = [&](const void* Yop, const void* Pop) {
+    GemmArgs g;
+    if (b.tall) {
+      g = gemm_args(T, cnt, (int)n, (int)m, (int)m, false);
+      g.L = Yop; g.ldl = b.mp; g.sL = sy;
+      g.R = Pop; g.ldr = b.mp; g.sR = ss;
+    } else {
+      g = gemm_args(T, cnt, (int)m, (int)n, (int)m, false);
+      g.L = Pop; g.ldl = b.mp; g.sL = ss;
+      g.R = Yop; g.ldr = b.mp; g.sR = sy;
+    }
     g.desc = d_desc;
     g.lr = cp.lr;
     g.wd = cp.wd;
     g.finalMode = cp.final_mode;
-    g.tall = b.tall;
+    g.tall = 1;  // output tiles in the parameter block's layout
     g.wvec = cp.wvec;
+    return g;
   };
   // symmetric product L . R^T of m x m output into C (both triangles)
   auto sym_args = [&](const void* L, int64_t ldl, int64_t sL, const void* R, int64_t ldr, int64_t sR,
@@ -159,19 +175,22 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
       g.alpha = cc; g.beta = cb; g.gamma = ca;
       HIP_TRY(timed(F_POLY, mmm, 0.0, st,
                     [&] { return launch_gemm(T, cdt, cdt, true, EPI_POLY, false, g, st); }));
-      // Y' = Y P^T  (k = 0: (P U)^T / s)
-      g = gemm_args(T, cnt, (int)n, (int)m, (int)m, false);
-      g.L = Y[k & 1]; g.ldl = b.mp; g.sL = sy;
-      g.R = B; g.ldr = b.mp; g.sR = ss;
+      // Y' = Y P^T  (k = 0: (P U)^T / s); the last one fused with the update
+      if (k + 1 < cp.steps) {
+        g = gemm_args(T, cnt, (int)n, (int)m, (int)m, false);
+        g.L = Y[k & 1]; g.ldl = b.mp; g.sL = sy;
+        g.R = B; g.ldr = b.mp; g.sR = ss;
+        g.C = Y[(k + 1) & 1]; g.ldc = b.mp; g.sC = sy;
+      } else {
+        g = final_gemm(Y[k & 1], B);
+      }
       g.alpha = 1.f; g.beta = 0.f;
       g.alphaSel = k == 0 ? SEL_INV_S : SEL_ONE;
       g.aux = d_aux;
       if (k + 1 < cp.steps) {
-        g.C = Y[(k + 1) & 1]; g.ldc = b.mp; g.sC = sy;
         HIP_TRY(timed(F_UPDATE, mm_n, 0.0, st,
                       [&] { return launch_gemm(T, cdt, cdt, false, EPI_SCALE, false, g, st); }));
       } else {
-        final_args(g);
         HIP_TRY(timed(F_FINAL, mm_n, elems * 2.0 * pes, st,
                       [&] { return launch_gemm(T, cdt, pdt, false, EPI_FINAL, false, g, st); }));
       }
@@ -235,13 +254,10 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
     }
   }
   // O^T = Y0 Q^T / s  (= (Q X0)^T / s), fused with the update
-  g = gemm_args(T, cnt, (int)n, (int)m, (int)m, false);
-  g.L = Y0; g.ldl = b.mp; g.sL = sy;
-  g.R = PZ[z]; g.ldr = b.mp; g.sR = ss;
+  g = final_gemm(Y0, PZ[z]);
   g.beta = 0.f;
   g.alphaSel = SEL_INV_S;
   g.aux = d_aux;
-  final_args(g);
   HIP_TRY(timed(F_FINAL, mm_n, elems * 2.0 * pes, st,
                 [&] { return launch_gemm(T, cdt, pdt, false, EPI_FINAL, false, g, st); }));
   return MUON_OK;
