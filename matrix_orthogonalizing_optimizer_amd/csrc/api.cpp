@@ -141,7 +141,6 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
     g.lr = cp.lr;
     g.wd = cp.wd;
     g.finalMode = cp.final_mode;
-    g.tall = 1;  // output tiles in the parameter block's layout
     g.wvec = cp.wvec;
     return g;
   };

@@ -46,9 +46,9 @@
 // Epilogue: each wave stages its accumulators in LDS one 32-row strip at a
 // time, reads the strip back as 16-byte row pieces, turns them into output
 // values (scale; polynomial with the addend E read from global memory one
-// strip ahead; or the fused parameter update), and stores them as row chunks
-// (direct pass, to C) and/or transposed (mirror pass, to C2: the symmetric
-// mirror, or the transposed parameter block of a wide unit).
+// strip ahead; or the fused parameter update, whose tile is a tile of the
+// parameter block), and stores them as row chunks (direct pass, to C or the
+// parameter) and/or transposed (mirror pass, to C2: the symmetric mirror).
 #pragma once
 
 #include <type_traits>
@@ -591,12 +591,10 @@ void gemm_kernel(const GemmArgs a) {
   }
   const bool store_only = a.finalMode == FINAL_STORE;
   const bool diag = SYM && bi == bj;
-  // FINAL: the tile is O^T (rows: the unit's n index, columns: its m index);
-  // a tall unit's parameter block has that layout, a wide unit's the transposed one
-  const bool fdirect = EPI == EPI_FINAL && a.tall;
-  const bool fmirror = EPI == EPI_FINAL && !a.tall;
+  // FINAL: the tile is a tile of the parameter block (O^T = Y P^T for a tall
+  // unit, O = P X for a wide one), written by the direct pass
   const bool wpre = EPI == EPI_FINAL && !store_only && a.wvec != 0;
-  const bool mirror = EPI == EPI_FINAL ? fmirror : C2p != nullptr;
+  const bool mirror = EPI != EPI_FINAL && C2p != nullptr;
   float* strip = reinterpret_cast<float*>(&ring[0][0]) + wid * (32 * SROW);
   const int gc0 = col0 + wn * WN;  // global column of strip column 0
 
@@ -632,32 +630,23 @@ void gemm_kernel(const GemmArgs a) {
   };
   if constexpr (EPI == EPI_POLY) load_e(0, pe[0]);
 
-  // EPI_FINAL: the old parameter values of strip i at the positions of the
-  // pass that writes them, loaded like E one strip ahead.  A per-strip buffer
-  // resource starts at the strip's first parameter row, so offsets stay
-  // small whatever the parameter's size; pieces not wholly inside the block
-  // stay zero here and take the element-wise path, which reads W itself.
+  // EPI_FINAL: the old parameter values of strip i at the direct pass's
+  // positions, loaded like E one strip ahead.  A per-strip buffer resource
+  // starts at the strip's first parameter row, so offsets stay small
+  // whatever the parameter's size; pieces not wholly inside the block stay
+  // zero here and take the element-wise path, which reads W itself.
   Raw8<TO> pwb[2][NT];
   auto load_w = [&](int i, Raw8<TO>(&dst)[NT]) {
-    const int gri = row0 + wm * (BM / 2) + i * 32;
-    const int prow0 = fdirect ? gri : gc0;  // first parameter row the strip writes
-    const int prow_lim = fdirect ? a.M : a.N, pcol_lim = fdirect ? a.N : a.M;
-    const int rows_in = max(0, min(fdirect ? 32 : WN, prow_lim - prow0));
-    const TO* base = reinterpret_cast<const TO*>(d.w) + (int64_t)min(prow0, prow_lim) * d.ld;
+    const int prow0 = row0 + wm * (BM / 2) + i * 32;  // first parameter row of the strip
+    // uniform, but the compiler clamps it with a vector instruction: back to
+    // a scalar register, or the resource counts as divergent
+    const int rows_in = __builtin_amdgcn_readfirstlane(max(0, min(32, a.M - prow0)));
+    const TO* base = reinterpret_cast<const TO*>(d.w) + (int64_t)min(prow0, a.M) * d.ld;
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(base, (uint32_t)((int64_t)rows_in * d.ld * (int64_t)sizeof(TO)));
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      int r, c;  // parameter row (from prow0) and first column of piece t
-      if (fdirect) {
-        r = dr0 + DRS * t;
-        c = gj;
-      } else {
-        int jj, c8;
-        mpos(t, jj, c8);
-        r = jj;
-        c = gri + c8;
-      }
-      const uint32_t off = wpre && c + 8 <= pcol_lim ? (uint32_t)(((int64_t)r * d.ld + c) * (int64_t)sizeof(TO)) : OOB;
+      const int r = dr0 + DRS * t, c = gj;  // parameter row (from prow0) and first column of piece t
+      const uint32_t off = wpre && c + 8 <= a.N ? (uint32_t)(((int64_t)r * d.ld + c) * (int64_t)sizeof(TO)) : OOB;
 #pragma unroll
       for (int h = 0; h < (int)(sizeof(TO) / 2); ++h)
         dst[t].w[h] = __builtin_amdgcn_raw_buffer_load_b128(wrs, off + 16 * h, 0, 0);
@@ -736,7 +725,7 @@ void gemm_kernel(const GemmArgs a) {
       }
     }
     if constexpr (EPI == EPI_FINAL) {
-      if (fdirect && gj < a.N) {
+      if (gj < a.N) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           const int gi = gr0 + dr0 + DRS * t;
@@ -783,15 +772,7 @@ void gemm_kernel(const GemmArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) mv[t][e] = strip[(c8 + e) * SROW + jj];
       }
-      if constexpr (EPI == EPI_FINAL) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          int jj, c8;
-          mpos(t, jj, c8);
-          const int orow = gc0 + jj, ocol = gr0 + c8;
-          if (orow < a.N && ocol < a.M) final8(pw[t], orow, ocol, a.M, mv[t]);  // wide unit: parameter row orow
-        }
-      } else if (!diag) {
+      if (!diag) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           int jj, c8;

@@ -27,8 +27,6 @@ struct GemmArgs {
   const UnitDesc* desc;    // EPI_FINAL: per-unit parameter pointers
   float lr, wd;            // EPI_FINAL
   int32_t finalMode;       // FINAL_UPDATE or FINAL_STORE
-  int32_t tall;            // EPI_FINAL: 1 = output tiles in the parameter block's layout (direct
-                           // pass); 0 = its transpose (mirror pass)
   int32_t wvec;            // EPI_FINAL: parameter / update_out rows are 16-byte aligned, ld % 8 == 0
 };
 
