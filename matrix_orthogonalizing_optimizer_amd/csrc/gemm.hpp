@@ -401,11 +401,31 @@ void gemm_kernel(const GemmArgs a) {
   const int c0op = copiesL ? row0 : col0;
   const __amdgpu_buffer_rsrc_t rsrc =
       make_rsrc(P, (uint32_t)((int64_t)(TRANS ? a.K : prows) * ld * ES));
+  // 16-bit K-major copies: copy q fills RPC K-rows; a lane's K-row and chunk
+  // depend on q only through q & 1 (the chunk swizzle follows k & 3, and
+  // 2 * NQ * RPC is a multiple of 4), so each lane keeps two base offsets,
+  // and a copy adds the uniform part (q - (q & 1)) RPC + k0 rows.  Rows at or
+  // past K fall outside the resource; a lane whose column is past the
+  // operand starts at 2^31, past the resource at every stage (a wrap past
+  // 2^32 in the zero-filled stages after the last one reaches only columns
+  // whose output rows are dropped).
+  constexpr int RPC = 64 / CR;  // K-rows per copy
+  uint32_t tb[2] = {0u, 0u};
+  if constexpr (TRANS && ES == 2) {
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int krow = ((wid & 1) * NQ + par) * RPC + lane / CR;
+      const int col = c0op + ((lane % CR) ^ swz_t(krow)) * EPC;
+      tb[par] = col < prows ? (uint32_t)(((int64_t)krow * ld + col) * ES) : 0x80000000u;
+    }
+  }
 
   auto copy_one = [&](int q, int stage) {
     const int k0 = stage * BK;
     uint32_t off;
-    if constexpr (TRANS) {
+    if constexpr (TRANS && ES == 2) {
+      off = tb[q & 1] + (uint32_t)(((int64_t)((q & ~1) * RPC + k0) * ld) * ES);
+    } else if constexpr (TRANS) {
       const int slot = ((wid & 1) * NQ + q) * 64 + lane;
       const int krow = slot / CR;
       const int lc = (slot % CR) ^ swz_t(krow);
