@@ -433,10 +433,13 @@ void gemm_kernel(const GemmArgs a) {
       const bool ok = (k0 + krow < a.K) && (col < prows);
       off = ok ? (uint32_t)(((int64_t)(k0 + krow) * ld + col) * ES) : OOB;
     } else {
+      // rows past the operand fall outside the resource; a chunk past K
+      // (which could reach into the next row) starts at 2^31, past it too.
+      // The base depends on the stage and q & 1 only, so it is shared by
+      // the copies of one stage.
       const int ck = (q & 1) ? ck1 : ck0;
-      const uint32_t cb = (q & 1) ? cb1 : cb0;
-      const bool ok = (k0 + ck < a.K) && (crow + 8 * q < prows);
-      off = ok ? cb + (uint32_t)(k0 * ES) + (uint32_t)q * cstep : OOB;
+      const uint32_t base = k0 + ck < a.K ? ((q & 1) ? cb1 : cb0) + (uint32_t)(k0 * ES) : 0x80000000u;
+      off = base + (uint32_t)q * cstep;
     }
     copy16_to_lds(rsrc, &ring[stage % NSTG][slot_off + q * 64], off);
   };
