@@ -103,8 +103,8 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
   ma.partials = d_part;
   ma.rows = (int32_t)(b.tall ? n : m);
   ma.cols = (int32_t)(b.tall ? m : n);
-  ma.tilesR = (int32_t)ceil_div(ma.rows, KM_TR);
-  ma.tilesC = (int32_t)ceil_div(ma.cols, KM_TC);
+  ma.tilesR = (int32_t)ceil_div(ma.rows, b.tall ? KMR_TR : KM_TR);
+  ma.tilesC = (int32_t)ceil_div(ma.cols, b.tall ? KMR_TC : KM_TC);
   ma.tilesPerUnit = b.km_tiles;
   ma.mu = cp.mu;
   ma.nesterov = cp.nesterov;

@@ -148,6 +148,84 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MomArgs a) {
   if (tid == 0) a.partials[blockIdx.x] = s;
 }
 
+// The same for a tall unit, whose parameter block already has the working
+// layout (U is written as is): row-contiguous 8 x 512 tiles, each wave
+// covering 512 consecutive columns of one row (1 KB of a 16-bit G, 2 KB of
+// M), so that a workgroup's accesses fall in few DRAM pages.  One partial
+// sum of U^2 per workgroup.
+template <typename TG, typename TX>
+__global__ __launch_bounds__(256) void momentum_rows_kernel(const MomArgs a) {
+  static_assert(KMR_TR == 8 && KMR_TC == 512, "tile shape");
+  __shared__ float red[4];
+  const int unit = blockIdx.x / a.tilesPerUnit;
+  const int t = blockIdx.x - unit * a.tilesPerUnit;
+  const int tr = t / a.tilesC, tc = t - tr * a.tilesC;
+  const UnitDesc d = a.desc[unit];
+  const TG* __restrict__ G = reinterpret_cast<const TG*>(d.g);
+  float* __restrict__ M = d.mom;
+  TX* __restrict__ X = reinterpret_cast<TX*>(a.D) + (int64_t)unit * a.sD;
+
+  const int tid = threadIdx.x;
+  const int c = tc * KMR_TC + (tid & 63) * 8;
+  const bool cin = c < a.cols;
+  const bool full = a.vec_ok && c + 8 <= a.cols;
+  float g[2][8], m[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = tr * KMR_TR + (tid >> 6) + 4 * h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { g[h][e] = 0.f; m[h][e] = 0.f; }
+    if (r < a.rows && cin) {
+      const int64_t off = (int64_t)r * d.ld + c;
+      if (full) {
+        ld8(G + off, g[h]);
+        if (M) ld8(M + off, m[h]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (c + e < a.cols) {
+            g[h][e] = to_f32(G[off + e]);
+            if (M) m[h][e] = M[off + e];
+          }
+        }
+      }
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = tr * KMR_TR + (tid >> 6) + 4 * h;
+    float u[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (M) {
+        const float mn = fmaf(a.mu, m[h][e], g[h][e]);
+        m[h][e] = mn;
+        u[e] = a.nesterov ? fmaf(a.mu, mn, g[h][e]) : mn;
+      } else {
+        u[e] = g[h][e];
+      }
+      ss = fmaf(u[e], u[e], ss);
+    }
+    if (r < a.rows && cin) {
+      const int64_t off = (int64_t)r * d.ld + c;
+      if (M) {
+        if (full) {
+          st8(M + off, m[h]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (c + e < a.cols) M[off + e] = m[h][e];
+        }
+      }
+      // columns past cols within the chunk are the layout's zero padding
+      st8(X + (int64_t)r * a.ldd + c, u);
+    }
+  }
+  const float s = block_sum_256(ss, red);
+  if (tid == 0) a.partials[blockIdx.x] = s;
+}
+
 // Per-unit norm: sums the unit's partials in a fixed order and stores
 // {s^2, 1/s, 1/s^2, 0}.  A zero unit gets 1/s = 0 so its update is zero
 // ("Newton-Schulz Iteration": G <- G / ||G||_F; the page prints no epsilon).

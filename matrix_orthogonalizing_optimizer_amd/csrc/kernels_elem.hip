@@ -14,10 +14,20 @@ hipError_t launch_gemm(int tile, int ti, int to, bool sym, int epi, bool trans, 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_momentum(int gdtype, int xdtype, bool /*tall*/, const MomArgs& a, int64_t blocks,
+hipError_t launch_momentum(int gdtype, int xdtype, bool tall, const MomArgs& a, int64_t blocks,
                            hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   const dim3 g((unsigned)blocks), b(256);
+  if (tall) {
+    // the working layout is the parameter's own: row-contiguous tiles
+    if (a.D == nullptr) return hipErrorInvalidValue;
+    if (gdtype == DT_BF16 && xdtype == DT_BF16) hipLaunchKernelGGL((momentum_rows_kernel<bf16, bf16>), g, b, 0, s, a);
+    else if (gdtype == DT_F32 && xdtype == DT_F32) hipLaunchKernelGGL((momentum_rows_kernel<float, float>), g, b, 0, s, a);
+    else if (gdtype == DT_BF16 && xdtype == DT_F32) hipLaunchKernelGGL((momentum_rows_kernel<bf16, float>), g, b, 0, s, a);
+    else if (gdtype == DT_F32 && xdtype == DT_BF16) hipLaunchKernelGGL((momentum_rows_kernel<float, bf16>), g, b, 0, s, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   if (gdtype == DT_BF16 && xdtype == DT_BF16) hipLaunchKernelGGL((momentum_kernel<bf16, bf16>), g, b, 0, s, a);
   else if (gdtype == DT_F32 && xdtype == DT_F32) hipLaunchKernelGGL((momentum_kernel<float, float>), g, b, 0, s, a);
   else if (gdtype == DT_BF16 && xdtype == DT_F32) hipLaunchKernelGGL((momentum_kernel<bf16, float>), g, b, 0, s, a);

@@ -49,7 +49,8 @@ void bucket_derive(PlanBucket& b, size_t chunk_cap_bytes) {
   b.tile = b.m <= 192 ? 128 : 256;
   // momentum kernel tiles over the unit in parameter layout
   const int64_t prow = b.tall ? b.n : b.m, pcol = b.tall ? b.m : b.n;
-  b.km_tiles = (int32_t)(((prow + KM_TR - 1) / KM_TR) * ((pcol + KM_TC - 1) / KM_TC));
+  const int64_t ktr = b.tall ? KMR_TR : KM_TR, ktc = b.tall ? KMR_TC : KM_TC;
+  b.km_tiles = (int32_t)(((prow + ktr - 1) / ktr) * ((pcol + ktc - 1) / ktc));
   const size_t per = per_unit_data_bytes(b);
   int64_t chunk = (int64_t)(chunk_cap_bytes / std::max<size_t>(per, 1));
   chunk = std::max<int64_t>(1, std::min<int64_t>(chunk, b.count));
