@@ -6,13 +6,15 @@
 // and "Newton-Schulz Iteration"):
 //   K-M    M <- mu M + G;  U = G + mu M (Nesterov) or M;  Y0 = U^T of the wide
 //          orientation (a tall parameter block already has that layout)
-//          and partial sums of U^2                      [momentum_kernel]
+//          and partial sums of U^2  [momentum_kernel: wide; momentum_rows_kernel: tall]
 //   norm   s^2 per unit, 1/s, 1/s^2                      [norm_finalize_kernel]
 //   k = 0..steps-1 with (a_k, b_k, c_k):
 //     A = X X^T            (k = 0: times 1/s^2, folding X0 = U / s)
 //     P = a I + b A + c A A (symmetric: upper tiles, mirror-written)
 //     X' = P X = a X + (b A + c A^2) X   (k = 0: times 1/s), computed as
-//                          Y' = Y P^T on the transposed copy; the last step's
+//                          Y' = Y P^T on the transposed copy; the last step
+//                          is computed in the parameter's layout (O^T = Y P^T
+//                          for a tall unit, O = P Y^T for a wide one) and its
 //                          epilogue applies W <- W (1 - lr wd) - lr scale O
 // Gram method (DeepSpeed page: iterate on the square Gram matrix R = X X^T):
 //   R = 2^e X0 X0^T / s^2 (power-of-two scaled, fp16 for a bf16 bucket);
@@ -252,7 +254,7 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
                     [&] { return launch_gemm(T, sdt, sdt, true, EPI_SCALE, false, g, st); }));
     }
   }
-  // O^T = Y0 Q^T / s  (= (Q X0)^T / s), fused with the update
+  // O = Q X0 / s (O^T = Y0 Q^T / s for a tall unit), fused with the update
   g = final_gemm(Y0, PZ[z]);
   g.beta = 0.f;
   g.alphaSel = SEL_INV_S;
