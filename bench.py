@@ -271,11 +271,16 @@ GEMM_SOURCES = ("matrix_orthogonalizing_optimizer_amd/csrc/gemm.hpp",
 
 
 def gemm_source_digest() -> str:
+    """SHA-256 of the GEMM sources with // comments and whitespace removed, so
+    that only a change of code (not of its comments) invalidates counters."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        code = re.sub(r"//[^\n]*", "", text)
+        h.update("".join(code.split()).encode())
     return h.hexdigest()
 
 
