@@ -38,9 +38,9 @@
 // each step carry the fragment reads of the next; before the last step a
 // barrier (after this wave's copies of the next stage landed and its reads
 // of this stage completed) frees this stage's slot; the last step's MFMAs
-// carry copies of the stage after next into it (all of them for K-major
-// operands; half for row-major ones, whose other half ride on the first step
-// of the next stage) and the fragment reads of the next stage's first step.  A wave issues in order and an MFMA keeps the matrix pipe busy for
+// carry half of the copies of the stage after next into it (the other half
+// ride on the first step of the next stage; 256 x 256 tiles) and the
+// fragment reads of the next stage's first step.  A wave issues in order and an MFMA keeps the matrix pipe busy for
 // 32 cycles, so each memory instruction is placed between two MFMAs.
 //
 // Epilogue: each wave stages its accumulators in LDS one 32-row strip at a
@@ -509,17 +509,16 @@ void gemm_kernel(const GemmArgs a) {
     Mfma<TI>::run(acc[i][j], fa[slot][i], fb[slot][j]);
   };
 
-  // Row-major 256 x 256 products split the copies of a stage: half go out
-  // during the last step of the stage two before it (right after the barrier
-  // that frees its slot), one every other MFMA; the other half during the
-  // first step of the next stage, one per MFMA of its second half (the first
-  // half carries the fragment reads).  All of them land before the barrier
-  // that precedes that stage's last step.  Issuing all 16 copies back to
-  // back in one step (one per MFMA) measured 4-5% slower on the update
-  // (spreading the second half over two steps: 0.5% slower than this); the
-  // K-major product keeps that schedule, which measured 1-4% faster for it
-  // than the split ones.
-  constexpr bool SPLIT = !TRANS && NPAIR - NDR >= 8 && NQ == 16;
+  // 256 x 256 products split the copies of a stage: half go out during the
+  // last step of the stage two before it (right after the barrier that frees
+  // its slot), one every other MFMA; the other half during the first step of
+  // the next stage, one per MFMA of its second half (the first half carries
+  // the fragment reads).  All of them land before the barrier that precedes
+  // that stage's last step.  Issuing all 16 copies back to back in one step
+  // (one per MFMA) measured 4-5% slower on the update and on the K-major
+  // product (spreading the second half over two steps: 0.5% slower than
+  // this).
+  constexpr bool SPLIT = NPAIR - NDR >= 8 && NQ == 16;
   constexpr int NQ3 = SPLIT ? NQ / 2 : NQ;
   constexpr int NQR = NQ - NQ3;
   static_assert(!SPLIT || (NQ3 * 2 <= NPAIR && NQR <= NPAIR - NDR), "split copy slots");
