@@ -618,6 +618,15 @@ void gemm_kernel(const GemmArgs a) {
   const bool wpre = EPI == EPI_FINAL && !store_only && a.wvec != 0;
   const bool mirror = EPI != EPI_FINAL && C2p != nullptr;
   float* strip = reinterpret_cast<float*>(&ring[0][0]) + wid * (32 * SROW);
+  // 16-bit outputs: the direct pass also leaves its converted values in a
+  // 16-bit strip (rows RS16 bytes apart: the 4 rows a 16-lane transposed read
+  // touches fall on distinct LDS banks), from which the mirror pass takes a
+  // column's 8 values with two ds_read_b64_tr_b16: the mirror stores the very
+  // bits of the direct pass, and reads 2 instructions instead of 8
+  constexpr bool MIR16 = sizeof(TO) == 2;
+  constexpr int RS16 = WN * 2 + 32;
+  static_assert(4 * 32 * SROW * 4 + 4 * 32 * RS16 <= NSTG * STG * 16, "16-bit strips fit in the ring");
+  char* strip16 = reinterpret_cast<char*>(&ring[0][0]) + 4 * 32 * SROW * 4 + wid * (32 * RS16);
   const int gc0 = col0 + wn * WN;  // global column of strip column 0
 
   // Each pass covers the 32 x WN strip of MFMA row-tile i in NT rounds of 64
@@ -741,9 +750,16 @@ void gemm_kernel(const GemmArgs a) {
     if (mirror) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        float* sp = strip + (dr0 + DRS * t) * SROW + dc8;
-        *reinterpret_cast<f32x4*>(sp) = f32x4{v[t][0], v[t][1], v[t][2], v[t][3]};
-        *reinterpret_cast<f32x4*>(sp + 4) = f32x4{v[t][4], v[t][5], v[t][6], v[t][7]};
+        if constexpr (MIR16) {
+          u32x4 w;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) w[j] = pack2<TO>(v[t][2 * j], v[t][2 * j + 1]);
+          *reinterpret_cast<u32x4*>(strip16 + (dr0 + DRS * t) * RS16 + dc8 * 2) = w;
+        } else {
+          float* sp = strip + (dr0 + DRS * t) * SROW + dc8;
+          *reinterpret_cast<f32x4*>(sp) = f32x4{v[t][0], v[t][1], v[t][2], v[t][3]};
+          *reinterpret_cast<f32x4*>(sp + 4) = f32x4{v[t][4], v[t][5], v[t][6], v[t][7]};
+        }
       }
     }
     if constexpr (EPI == EPI_FINAL) {
@@ -784,7 +800,55 @@ void gemm_kernel(const GemmArgs a) {
     // mirror pass: strip column jj, rows c8..c8+7 -> row gc0 + jj of the
     // transposed output (rows of the output are the tile's columns, its
     // columns the tile's rows); all reads first, then the stores
-    if (mirror) {
+    if (mirror && MIR16) {
+      __syncthreads();  // values of the direct pass are in the 16-bit strip
+      // a 16-lane group covers 16 consecutive strip columns jj at one c8;
+      // lane 4e + q of it addresses row c8 + e (+4), columns 4q .. 4q + 3 of
+      // the group, and receives its own column's 4 rows
+      const int L = lane & 15;
+      u32x4 mw[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        int jj, c8;
+        mpos(t, jj, c8);
+        const char* p = strip16 + (c8 + (L >> 2)) * RS16 + (jj - L + 4 * (L & 3)) * 2;
+        const uint32_t addr = (uint32_t)(uintptr_t)(lds_ptr_t)p;
+        const uint2 lo = lds_read_tr16_off<0>(addr);
+        const uint2 hi = lds_read_tr16_off<4 * RS16>(addr);
+        mw[t] = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+      wait_lgkm0();  // the transposed reads are not tracked by the compiler
+      if (!diag) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          int jj, c8;
+          mpos(t, jj, c8);
+          const int orow = gc0 + jj, ocol = gr0 + c8;
+          // rows at or past N fall outside the resource
+          const uint32_t off = ocol < a.M ? (uint32_t)(((int64_t)orow * a.ldc2 + ocol) * (int64_t)sizeof(TO)) : OOB;
+          __builtin_amdgcn_raw_buffer_store_b128(mw[t], c2rs, off, 0, 0);
+        }
+      } else {
+        // diagonal tile of a symmetric product: strictly lower positions
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          int jj, c8;
+          mpos(t, jj, c8);
+          const int orow = gc0 + jj, ocol = gr0 + c8;
+          if (orow < a.N && ocol < a.M) {
+            TO* dst = C2p + (int64_t)orow * a.ldc2 + ocol;
+            if (ocol + 7 < orow) {
+              *reinterpret_cast<u32x4*>(dst) = mw[t];
+            } else {
+              uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (ocol + e < orow) d16[e] = (uint16_t)(mw[t][e >> 1] >> (16 * (e & 1)));
+            }
+          }
+        }
+      }
+    } else if (mirror) {
       __syncthreads();  // values of the direct pass are in the strip
       float mv[NT][8];
 #pragma unroll
