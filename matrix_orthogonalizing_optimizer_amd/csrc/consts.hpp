@@ -3,7 +3,7 @@
 
 namespace muon {
 constexpr int KM_TR = 64;       // momentum kernel tile rows (parameter layout)
-constexpr int KM_TC = 64;       // momentum kernel tile columns
+constexpr int KM_TC = 128;      // momentum kernel tile columns
 constexpr int KMR_TR = 8;       // momentum kernel tile rows, tall units (row-contiguous tiles)
 constexpr int KMR_TC = 512;     // momentum kernel tile columns, tall units
 constexpr int ADAM_EPB = 4096;  // AdamW elements per workgroup
