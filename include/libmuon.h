@@ -50,12 +50,18 @@ typedef enum {
   MUON_E_CAPACITY = -8   /* output array too small (query calls) */
 } muon_status;
 
-/* [DeepSpeed] NS_METHODS = {standard, gram}.  MUON_NS_AUTO picks per unit
- * (m = min, n = max of its sides): Gram where it does less work, n/m > 5/3
- * (executed cost with symmetric products: standard steps (3 m^2 n + m^3),
- * Gram 3 m^2 n + (6 steps - 5) m^3), and only for m >= 512, where its
- * power-of-two scaled fp16 chain stays within the bf16 tolerance; standard
- * otherwise.  Plans report the method each bucket resolved to. */
+/* [DeepSpeed] NS_METHODS = {standard, gram}: the standard iteration on the
+ * m x n unit, or the Gram variant, which iterates on the square R = X X^T
+ * (m = min, n = max of the unit's sides).  The Gram chain runs in fp16 with
+ * R scaled by a power of two only where that stays within the bf16
+ * tolerance on the workload gradients, m >= 512 and n >= 3m; a Gram unit
+ * outside that region with a 16-bit compute dtype computes in fp32 instead
+ * (its bucket reports compute dtype MUON_F32), so MUON_NS_GRAM never trades
+ * accuracy for speed silently.  MUON_NS_AUTO picks Gram exactly in that
+ * region, where it also does less work (executed cost with symmetric
+ * products: standard steps (3 m^2 n + m^3), Gram 3 m^2 n + (6 steps - 5)
+ * m^3, so Gram is cheaper for n/m > 5/3), and the standard method
+ * elsewhere.  Plans report the method and compute dtype of every bucket. */
 typedef enum { MUON_NS_STANDARD = 0, MUON_NS_GRAM = 1, MUON_NS_AUTO = 2 } muon_ns_method;
 
 /* Storage dtype of parameters and gradients.  Momentum and AdamW moments are
@@ -165,19 +171,34 @@ typedef struct {
 
 typedef struct muon_plan muon_plan;
 
-/* Build an immutable plan from a shape table of n rows: units (one per
- * matrix or row block) grouped into buckets of equal (m, n, tall, parameter
+/* Build an immutable plan from a shape table of n rows (table: host array
+ * owned by the caller, read only during the call): units (one per matrix
+ * or row block) grouped into buckets of equal (m, n, tall, parameter
  * dtype, compute dtype, method), m = min and n = max of the unit's sides.
+ * Which parameters take the Muon rule and which the AdamW backup follows
+ * [Moonlight] "代码" (use_muon; Muon only for 2-D weights); a split
+ * parameter's row blocks are orthogonalized independently, as the fused QKV
+ * weight is in [MindSpeed] "TP 兼容适配" (Q, K, V blocks) and per attention
+ * head in [DeepSpeed] (Muon Split); a tall unit is processed as its
+ * transpose ([Blog] "Sign of a Matrix": msign(G) = G (G^T G)^(-1/2)).
  * Buckets are numbered by first appearance; units keep table order.  Host
- * only (no HIP call).  *out receives a heap object to release with
+ * only (no HIP call).  opts may be NULL (standard method, compute dtype of
+ * the parameters).  *out receives a heap object to release with
  * muon_plan_destroy.  Errors: MUON_E_ARG (null out, n < 0, unknown kind),
  * MUON_E_DTYPE, MUON_E_METHOD, MUON_E_SHAPE (negative size, side > 2^30,
- * split_rows not dividing rows or set on an AdamW row). */
+ * split_rows not dividing rows or set on an AdamW row, a unit whose
+ * working copy reaches 2^31 bytes); on error *out is NULL. */
 muon_status muon_plan_create(const muon_param_shape* table, int32_t n,
                              const muon_plan_options* opts, muon_plan** out);
 void muon_plan_destroy(muon_plan* plan);
 
-/* Bytes of device workspace muon_step needs with this plan. */
+/* Bytes of device workspace muon_step needs with this plan (host only).
+ * The workspace holds, per bucket chunk, the working copies of the
+ * Newton-Schulz iteration ([Blog] "Newton-Schulz Iteration": X and its
+ * transpose-side products A = X X^T and P = aI + bA + cA^2, or the Gram
+ * variant's R, P and Q of [DeepSpeed]), the per-unit norms and the device
+ * descriptor tables.  0 for a plan without units or AdamW parameters.
+ * Errors: MUON_E_ARG (null plan or bytes). */
 muon_status muon_plan_workspace_bytes(const muon_plan* plan, size_t* bytes);
 
 /* Bit-exact view of the plan (host only).  Buckets: 8 int32 per bucket
@@ -190,16 +211,46 @@ muon_status muon_plan_buckets(const muon_plan* plan, int32_t* out, size_t cap, s
 muon_status muon_plan_units(const muon_plan* plan, int64_t* out, size_t cap, size_t* len);
 
 /* One optimizer step for every parameter of the plan's table (n must equal
- * the table size).  Enqueues on stream; all state is updated in place. */
+ * the table size; ptrs: host array of n entries in table order, read only
+ * during the call; hp: host struct, read only during the call).
+ * Per Muon unit ([Blog] "Formulation of Muon Optimizer" and "Newton-Schulz
+ * Iteration"; [Moonlight] "权重衰减机制", "参数更新尺度调整" and "代码"):
+ *   M <- mu M + G;  U = G + mu M (nesterov) or M;  X0 = U / ||U||_F;
+ *   X <- a_k X + (b_k A + c_k A^2) X, A = X X^T, k = 0 .. ns_steps-1
+ *     (or the Gram variant of [DeepSpeed]);
+ *   W <- W (1 - lr wd) - lr scale O, scale per muon_scale_mode;
+ * a unit whose U is zero gets O = 0 (its weight only decays).  Per AdamW
+ * parameter: the AdamW backup of [Moonlight] "代码" (see muon_hparams).
+ * param, momentum, exp_avg, exp_avg_sq are updated in place and update_out
+ * written; grad is read only.  workspace: device memory of at least
+ * muon_plan_workspace_bytes bytes, owned by the caller; its contents need
+ * not be initialized and are scratch between calls.  The per-unit
+ * descriptors reach the workspace through the arguments of small kernel
+ * launches (3 KiB each), not through a host-to-device copy, so the call
+ * only enqueues work on stream (a hipStream_t, NULL = default stream) and
+ * returns without waiting for the GPU.  Errors, all before the first
+ * launch: MUON_E_PLAN (n
+ * differs from the table), MUON_E_ARG (null plan, hp or ptrs; a required
+ * pointer null or misaligned; a non-finite or out-of-range hparam),
+ * MUON_E_WORKSPACE; MUON_E_HIP if a HIP call fails. */
 muon_status muon_step(const muon_plan* plan, const muon_param_ptrs* ptrs, int32_t n,
                       const muon_hparams* hp, void* workspace, size_t workspace_bytes,
                       void* stream);
 
-/* Newton-Schulz orthogonalization of one matrix X (rows x cols, leading
- * dimension ld >= cols, dtype MUON_F32 or MUON_BF16), in place:
- * X <- NS_steps(X / ||X||_F), a tall X being processed as its transpose
- * ([Blog] "Sign of a Matrix", "Newton-Schulz Iteration").  coeffs as in
- * muon_hparams.  A zero matrix stays zero. */
+/* Newton-Schulz orthogonalization of one matrix X (device memory, rows x
+ * cols, leading dimension ld >= cols elements, dtype MUON_F32 or MUON_BF16),
+ * in place: X <- NS_steps(X / ||X||_F) ([Blog] "Newton-Schulz Iteration":
+ * X <- a_k X + (b_k A + c_k A^2) X with A = X X^T), a tall X being processed
+ * as its transpose ([Blog] "Sign of a Matrix"); method standard, Gram
+ * ([DeepSpeed]; fp32 outside the fp16 region described above) or auto.
+ * coeffs: host array of steps x 3 floats as in muon_hparams, or NULL.  A
+ * zero matrix stays zero.  workspace: device memory of at least
+ * ns_orthogonalize_workspace_bytes bytes, owned by the caller, contents
+ * need not be initialized.  Enqueues on stream and returns.  Errors, before
+ * any launch: MUON_E_DTYPE, MUON_E_METHOD, MUON_E_SHAPE (negative size,
+ * ld < cols, a side above 2^30 or a working copy of 2^31 bytes or more),
+ * MUON_E_ARG (X null or misaligned, steps out of [1, 64], a non-finite
+ * coefficient), MUON_E_WORKSPACE; MUON_E_HIP if a launch fails. */
 muon_status ns_orthogonalize(void* X, int64_t rows, int64_t cols, int64_t ld, int32_t dtype,
                              int32_t steps, const float* coeffs, int32_t method,
                              void* workspace, size_t workspace_bytes, void* stream);

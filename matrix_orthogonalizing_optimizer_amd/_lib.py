@@ -140,14 +140,46 @@ def _stream(stream) -> Optional[int]:
 
 
 def _coeff_array(coeffs, steps):
+    """Host array of steps x 3 floats for the library, or None (the quintic).
+    ``coeffs``: one (a, b, c) triple (used at every step) or exactly ``steps``
+    triples of finite numbers; anything else raises ValueError before the
+    library reads 3 * steps floats from it."""
     if coeffs is None:
         return None
-    flat = []
+    import math
     if len(coeffs) == 3 and not hasattr(coeffs[0], "__len__"):
-        coeffs = [coeffs] * steps
+        coeffs = [coeffs] * int(steps)
+    if len(coeffs) != steps:
+        raise ValueError(f"coeffs: {len(coeffs)} rows for {steps} Newton-Schulz steps")
+    flat = []
     for row in coeffs:
-        flat.extend(float(x) for x in row)
-    return (ctypes.c_float * len(flat))(*flat)
+        if not hasattr(row, "__len__") or len(row) != 3:
+            raise ValueError("coeffs: every row must be an (a, b, c) triple")
+        vals = [float(x) for x in row]
+        if not all(math.isfinite(v) for v in vals):
+            raise ValueError("coeffs: non-finite coefficient")
+        flat.extend(vals)
+    return (ctypes.c_float * max(len(flat), 3))(*flat)
+
+
+def _device_index(stream):
+    """Index of the GPU the call's kernels run on: the stream's device, or
+    the current device when the current stream is used."""
+    import torch
+    if stream is None or isinstance(stream, int):
+        return torch.cuda.current_device()
+    return stream.device.index
+
+
+def _check_device(name, t, device_index):
+    """A torch tensor handed to the library must live on the GPU the kernels
+    run on: its data_ptr() is used as a device address there."""
+    if t is None or isinstance(t, int) or not hasattr(t, "data_ptr"):
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name}: a {t.device} tensor; the library needs device memory")
+    if device_index is not None and t.device.index != device_index:
+        raise ValueError(f"{name}: on {t.device}, the kernels run on cuda:{device_index}")
 
 
 class Plan:
@@ -218,11 +250,12 @@ def make_hparams(lr=0.02, momentum=0.95, weight_decay=0.1, nesterov=True, ns_ste
     return hp
 
 
-def _check_buffer(name, t, rows, cols, dtype):
+def _check_buffer(name, t, rows, cols, dtype, device_index=None):
     """A torch tensor handed to muon_step must be the contiguous rows x cols
-    buffer of the table's dtype: the library addresses it from its pointer
-    and the table alone.  Raw integer pointers and None pass unchecked (the
-    library rejects a null pointer where one is required)."""
+    device buffer of the table's dtype, on the GPU the kernels run on: the
+    library addresses it from its pointer and the table alone.  Raw integer
+    pointers and None pass unchecked (the library rejects a null pointer
+    where one is required)."""
     if t is None or isinstance(t, int) or not hasattr(t, "data_ptr"):
         return
     import torch
@@ -231,6 +264,7 @@ def _check_buffer(name, t, rows, cols, dtype):
         raise ValueError(f"{name}: dtype {t.dtype}, the table says {want}")
     if t.numel() != rows * cols or not t.is_contiguous():
         raise ValueError(f"{name}: expected a contiguous {rows} x {cols} tensor, got {tuple(t.shape)}")
+    _check_device(name, t, device_index)
 
 
 def muon_step(plan: Plan, params, grads, moms, exp_avgs, exp_avg_sqs, hp: MuonHparams, workspace,
@@ -243,16 +277,25 @@ def muon_step(plan: Plan, params, grads, moms, exp_avgs, exp_avg_sqs, hp: MuonHp
                       ("exp_avg_sqs", exp_avg_sqs), ("update_outs", update_outs)):
         if lst is not None and len(lst) != n:
             raise ValueError(f"{name}: {len(lst)} entries for a table of {n}")
+    tensors = [t for lst in (params, grads, moms, exp_avgs, exp_avg_sqs, update_outs or [], [workspace])
+               for t in lst if t is not None and hasattr(t, "data_ptr")]
+    di = None
+    if tensors:
+        if not all(t.is_cuda for t in tensors):
+            bad = next(t for t in tensors if not t.is_cuda)
+            raise ValueError(f"muon_step: a {bad.device} tensor; the library needs device memory")
+        di = _device_index(stream)
+    _check_device("workspace", workspace, di)
     for i, (kind, dt, rows, cols, _split, _sd) in enumerate(plan.table):
-        _check_buffer(f"params[{i}]", params[i], rows, cols, dt)
-        _check_buffer(f"grads[{i}]", grads[i], rows, cols, dt)
+        _check_buffer(f"params[{i}]", params[i], rows, cols, dt, di)
+        _check_buffer(f"grads[{i}]", grads[i], rows, cols, dt, di)
         if kind == MUON_KIND_MUON:
-            _check_buffer(f"moms[{i}]", moms[i], rows, cols, MUON_F32)
+            _check_buffer(f"moms[{i}]", moms[i], rows, cols, MUON_F32, di)
             if update_outs is not None:
-                _check_buffer(f"update_outs[{i}]", update_outs[i], rows, cols, MUON_F32)
+                _check_buffer(f"update_outs[{i}]", update_outs[i], rows, cols, MUON_F32, di)
         else:
-            _check_buffer(f"exp_avgs[{i}]", exp_avgs[i], rows, cols, MUON_F32)
-            _check_buffer(f"exp_avg_sqs[{i}]", exp_avg_sqs[i], rows, cols, MUON_F32)
+            _check_buffer(f"exp_avgs[{i}]", exp_avgs[i], rows, cols, MUON_F32, di)
+            _check_buffer(f"exp_avg_sqs[{i}]", exp_avg_sqs[i], rows, cols, MUON_F32, di)
     arr = (MuonParamPtrs * max(n, 1))()
     for i in range(n):
         arr[i] = MuonParamPtrs(_ptr(params[i]), _ptr(grads[i]), _ptr(moms[i]), _ptr(exp_avgs[i]),
@@ -276,8 +319,13 @@ def ns_orthogonalize(X, steps: int = 5, coeffs=None, method: int = MUON_NS_STAND
                      stream=None, rows=None, cols=None, ld=None, dtype=None) -> None:
     """In place: X <- NewtonSchulz(X / ||X||_F).  X: a 2-D device tensor
     (fp32 or bf16, rows may be strided) or a raw pointer with rows/cols/ld/dtype."""
+    ca = _coeff_array(coeffs, steps)
     if hasattr(X, "data_ptr"):
         import torch
+        di = _device_index(stream) if X.is_cuda else None
+        _check_device("X", X, di)
+        if workspace is not None:
+            _check_device("workspace", workspace, di)
         if X.dim() != 2 or X.stride(1) != 1:
             raise ValueError("X must be 2-D with unit column stride")
         rows, cols = X.shape
@@ -288,7 +336,6 @@ def ns_orthogonalize(X, steps: int = 5, coeffs=None, method: int = MUON_NS_STAND
         if workspace is None:
             nb = ns_orthogonalize_workspace_bytes(rows, cols, dtype, method)
             workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=X.device)
-    ca = _coeff_array(coeffs, steps)
     wsz = workspace.numel() if hasattr(workspace, "numel") else 0
     if isinstance(workspace, tuple):
         workspace, wsz = workspace

@@ -466,10 +466,10 @@ muon_status muon_step(const muon_plan* plan, const muon_param_ptrs* ptrs, int32_
   }
   UnitDesc* d_desc = reinterpret_cast<UnitDesc*>(ws + P.lay.off_desc);
   AdamDesc* d_adesc = reinterpret_cast<AdamDesc*>(ws + P.lay.off_adesc);
-  if (!hd.empty())
-    HIP_TRY(hipMemcpyAsync(d_desc, hd.data(), hd.size() * sizeof(UnitDesc), hipMemcpyHostToDevice, st_));
-  if (!ad.empty())
-    HIP_TRY(hipMemcpyAsync(d_adesc, ad.data(), ad.size() * sizeof(AdamDesc), hipMemcpyHostToDevice, st_));
+  // descriptor tables travel in kernel arguments: no host staging, no copy
+  // from pageable memory, nothing the host waits for
+  if (!hd.empty()) HIP_TRY(launch_upload(d_desc, hd.data(), hd.size() * sizeof(UnitDesc), st_));
+  if (!ad.empty()) HIP_TRY(launch_upload(d_adesc, ad.data(), ad.size() * sizeof(AdamDesc), st_));
 
   ChainParams cp;
   cp.mu = hp->momentum;
@@ -534,8 +534,8 @@ static muon_status ns_bucket(int64_t rows, int64_t cols, int32_t dtype, int32_t 
   b.n = (int32_t)std::max(rows, cols);
   b.tall = rows > cols ? 1 : 0;
   b.pdtype = dtype;
-  b.cdtype = dtype;
   b.method = resolve_method(method, b.m, b.n);
+  b.cdtype = resolve_cdtype(dtype, b.method, b.m, b.n);
   b.first = 0;
   b.count = 1;
   bucket_derive(b, ~size_t(0));
@@ -585,7 +585,7 @@ muon_status ns_orthogonalize(void* X, int64_t rows, int64_t cols, int64_t ld, in
   d.o = nullptr;
   d.ld = ld;
   d.scale = 0.f;
-  HIP_TRY(hipMemcpyAsync(ws, &d, sizeof(d), hipMemcpyHostToDevice, st_));
+  HIP_TRY(launch_upload(ws, &d, sizeof(d), st_));
   ChainParams cp;
   cp.mu = 0.f;
   cp.nesterov = 0;

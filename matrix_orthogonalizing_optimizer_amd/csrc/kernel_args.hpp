@@ -53,4 +53,15 @@ struct AdamArgs {
   float one_minus_b1, one_minus_b2, eps, keep, step;
 };
 
+// Host table -> device memory through kernel arguments: one launch carries
+// up to BLOB_WORDS 32-bit words of a descriptor table, so no host staging
+// buffer, no host-to-device copy and no wait on the host are involved.
+constexpr int BLOB_WORDS = 768;  // 3 KiB of payload per launch
+struct BlobArgs {
+  uint32_t* dst;
+  uint32_t nwords;
+  uint32_t pad;
+  uint32_t words[BLOB_WORDS];
+};
+
 }  // namespace muon

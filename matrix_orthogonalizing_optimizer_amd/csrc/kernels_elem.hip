@@ -1,4 +1,6 @@
 // Launchers of the elementwise kernels and the GEMM dtype dispatch.
+#include <cstring>
+
 #include "elementwise.hpp"
 #include "launch.hpp"
 
@@ -41,6 +43,27 @@ hipError_t launch_norm_finalize(const float* partials, int32_t per_unit, float4*
   if (units <= 0) return hipSuccess;
   hipLaunchKernelGGL(norm_finalize_kernel, dim3(units), dim3(256), 0, s, partials, per_unit, aux);
   return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void upload_kernel(const BlobArgs a) {
+  for (uint32_t i = threadIdx.x; i < a.nwords; i += 256) a.dst[i] = a.words[i];
+}
+
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  if (bytes % 4 != 0 || reinterpret_cast<uintptr_t>(dst) % 4 != 0) return hipErrorInvalidValue;
+  const size_t words = bytes / 4;
+  BlobArgs a;
+  for (size_t w0 = 0; w0 < words; w0 += BLOB_WORDS) {
+    const size_t nw = words - w0 < (size_t)BLOB_WORDS ? words - w0 : (size_t)BLOB_WORDS;
+    a.dst = static_cast<uint32_t*>(dst) + w0;
+    a.nwords = (uint32_t)nw;
+    a.pad = 0;
+    std::memcpy(a.words, static_cast<const uint32_t*>(src) + w0, nw * 4);
+    hipLaunchKernelGGL(upload_kernel, dim3(1), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_adamw(const AdamArgs& a0, int64_t total_blocks, hipStream_t s) {

@@ -21,5 +21,9 @@ hipError_t launch_momentum(int gdtype, int xdtype, bool tall, const MomArgs& a, 
 hipError_t launch_norm_finalize(const float* partials, int32_t per_unit, float4* aux, int32_t units,
                                 hipStream_t s);
 hipError_t launch_adamw(const AdamArgs& a, int64_t total_blocks, hipStream_t s);
+// Writes `bytes` (a multiple of 4) from host memory src to device memory dst
+// (4-byte aligned) through the arguments of ceil(bytes / 3 KiB) small kernel
+// launches on s; src may be reused as soon as the call returns.
+hipError_t launch_upload(void* dst, const void* src, size_t bytes, hipStream_t s);
 
 }  // namespace muon

@@ -156,3 +156,65 @@ def plan(table, method: int = 0, ns_dtype: int = -1):
 # the numpy reference's names, so tests can run the same pins on both
 momentum_update = momentum
 adamw_update = adamw
+
+
+class Unit(tuple):
+    """(param, row0, rows, cols, tall, scale_dim) of one unit, with names."""
+    __slots__ = ()
+    param = property(lambda self: self[0])
+    row0 = property(lambda self: self[1])
+    rows = property(lambda self: self[2])
+    cols = property(lambda self: self[3])
+    tall = property(lambda self: bool(self[4]))
+    scale_dim = property(lambda self: self[5])
+
+
+def units_in_table_order(table):
+    """The C++ planner's units, listed parameter by parameter (row blocks in
+    ascending order) instead of bucket by bucket."""
+    units, _ = plan(table, 0, -1)
+    return [Unit(u) for u in sorted(units, key=lambda u: (u[0], u[1]))]
+
+
+def muon_step(table, params, grads, moms, exp_avgs, exp_avg_sqs, hp, method: str = "standard",
+              units_subset=None, want_updates: bool = False, adamw_params: bool = True):
+    """One optimizer step over a shape table with the C++ reference's
+    functions only (this is glue: every arithmetic step runs in
+    muon_ref.cpp).  Same arguments and result as the numpy reference's
+    ``muon_step``: ``hp`` carries lr, momentum, weight_decay, nesterov,
+    ns_steps, coeffs, rms_scale, scale_mode, extra_scale and the adam_*
+    fields; units are numbered in table order.  ``units_subset`` restricts
+    the Muon work to those units, and then only the parameters they touch
+    are copied (the others may be passed as None and come back as None);
+    ``adamw_params=False`` leaves the AdamW parameters out."""
+    units = units_in_table_order(table)
+    sel = list(range(len(units)) if units_subset is None else units_subset)
+    touched = {units[ui].param for ui in sel}
+    if adamw_params:
+        touched |= {p for p, row in enumerate(table) if row[0] == 1}
+    cp = lambda xs, p: None if xs[p] is None or p not in touched else _f64(xs[p]).copy()
+    W_out = [cp(params, p) for p in range(len(table))]
+    M_out = [cp(moms, p) for p in range(len(table))]
+    ea_out = [cp(exp_avgs, p) for p in range(len(table))]
+    es_out = [cp(exp_avg_sqs, p) for p in range(len(table))]
+    updates = {}
+    for ui in sel:
+        u = units[ui]
+        r0, r1 = u.row0, u.row0 + u.rows
+        M_new, U = momentum(_f64(moms[u.param])[r0:r1], _f64(grads[u.param])[r0:r1], hp.momentum,
+                            hp.nesterov)
+        M_out[u.param][r0:r1] = M_new
+        O = orthogonalize(U, hp.ns_steps, hp.coeffs, method)
+        scale = muon_scale(u.rows, u.cols, u.scale_dim, hp.rms_scale, hp.scale_mode, hp.extra_scale)
+        W_out[u.param][r0:r1] = weight_update(_f64(params[u.param])[r0:r1], O, hp.lr, hp.weight_decay,
+                                              scale)
+        if want_updates:
+            updates[ui] = O
+    for p, row in enumerate(table):
+        if row[0] != 1 or not adamw_params:
+            continue
+        W_out[p], ea_out[p], es_out[p] = adamw(params[p], grads[p], exp_avgs[p], exp_avg_sqs[p],
+                                               hp.adam_step, hp.adam_lr, hp.adam_beta1, hp.adam_beta2,
+                                               hp.adam_eps, hp.adam_weight_decay)
+    return {"W": W_out, "M": M_out, "exp_avg": ea_out, "exp_avg_sq": es_out, "O": updates,
+            "units": units}

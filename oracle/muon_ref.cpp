@@ -262,9 +262,14 @@ int64_t ref_plan(const int64_t* table, int32_t n, int32_t method, int32_t ns_dty
     const U& u = order[i];
     const int64_t pdt = table[6 * u.p + 1];
     const int64_t m = std::min(u.rows, u.cols), nn = std::max(u.rows, u.cols);
-    // method 2: Gram where it executes less work (n/m > 5/3) and m >= 512
-    const int64_t meth = method == 2 ? ((3 * nn > 5 * m && m >= 512) ? 1 : 0) : method;
-    const std::vector<int64_t> key = {m, nn, u.tall, pdt, ns_dtype < 0 ? pdt : ns_dtype, meth};
+    // Gram's fp16 chain is within the bf16 tolerance only for m >= 512 and
+    // n >= 3m: method 2 picks Gram there (where it also does less work), and
+    // a Gram unit outside it computes in fp32 (dtype code 0)
+    const bool fp16_ok = m >= 512 && nn >= 3 * m;
+    const int64_t meth = method == 2 ? (fp16_ok ? 1 : 0) : method;
+    int64_t cdt = ns_dtype < 0 ? pdt : ns_dtype;
+    if (meth == 1 && cdt == 1 && !fp16_ok) cdt = 0;
+    const std::vector<int64_t> key = {m, nn, u.tall, pdt, cdt, meth};
     size_t b = 0;
     while (b < keys.size() && keys[b] != key) ++b;
     if (b == keys.size()) {

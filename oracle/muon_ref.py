@@ -278,21 +278,38 @@ def plan_units(table) -> List[OracleUnit]:
     return units
 
 
+def gram_fp16_ok(m: int, n: int) -> bool:
+    """Where the Gram variant's power-of-two scaled fp16 chain stays within
+    the bf16 tolerance on the workload gradients: m >= 512 and n >= 3 m
+    (a rounding emulation of that chain gave 5.3e-2 at 512 x 860, 5.8e-2 at
+    768 x 768 and 3.5e-2 at 256 x 512, at most 1.25e-2 inside).  The pages
+    give no rule; this is the reading taken."""
+    return m >= 512 and n >= 3 * m
+
+
 def resolve_method(method: int, m: int, n: int) -> int:
-    """Method 2 ("auto") picks, per unit, the Gram variant where it executes
-    less work -- standard: steps (3 m^2 n + m^3) with symmetric products,
-    Gram: 3 m^2 n + (6 steps - 5) m^3, so n/m > 5/3 -- and only for m >= 512,
-    where its fp16 chain stays inside the bf16 tolerance (measured); the
-    standard method otherwise.  The pages give no rule; this is the reading
-    taken."""
+    """Method 2 ("auto") picks, per unit, the Gram variant where its fp16
+    chain is accurate (``gram_fp16_ok``), which also lies where it executes
+    less work than the standard method (standard: steps (3 m^2 n + m^3) with
+    symmetric products, Gram: 3 m^2 n + (6 steps - 5) m^3, i.e. n/m > 5/3);
+    the standard method otherwise."""
     if method != 2:
         return method
-    return 1 if (3 * n > 5 * m and m >= 512) else 0
+    return 1 if gram_fp16_ok(m, n) else 0
+
+
+def resolve_compute_dtype(dt: int, method: int, m: int, n: int) -> int:
+    """A Gram unit outside ``gram_fp16_ok`` computes in fp32 (code 0) instead
+    of bf16 (code 1), so that an explicit request for the Gram variant never
+    leaves the tolerance."""
+    if method == 1 and dt == DT_BF16 and not gram_fp16_ok(m, n):
+        return DT_F32
+    return dt
 
 
 def plan_buckets(table, method: int, ns_dtype: int = -1):
     """Group units with the same (m, n, tall, parameter dtype, compute dtype,
-    method).  Buckets are numbered by first appearance; units inside a bucket
+    method), the compute dtype as ``resolve_compute_dtype`` sets it.  Buckets are numbered by first appearance; units inside a bucket
     keep table order.  Brute force: for every unit, scan the buckets seen so
     far.  ``ns_dtype`` -1 means the compute dtype follows the parameter
     dtype."""
@@ -301,8 +318,9 @@ def plan_buckets(table, method: int, ns_dtype: int = -1):
     members = []
     for ui, u in enumerate(units):
         pdt = table[u.param][1]
-        dt = pdt if ns_dtype < 0 else ns_dtype
-        key = (u.m, u.n, 1 if u.tall else 0, pdt, dt, resolve_method(method, u.m, u.n))
+        meth = resolve_method(method, u.m, u.n)
+        dt = resolve_compute_dtype(pdt if ns_dtype < 0 else ns_dtype, meth, u.m, u.n)
+        key = (u.m, u.n, 1 if u.tall else 0, pdt, dt, meth)
         found = -1
         for bi, k in enumerate(keys):
             if k == key:

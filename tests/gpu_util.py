@@ -55,3 +55,25 @@ def hp_from(d: dict, adam_step: int = 1, coeffs=None):
                            adam_lr=d["adam_lr"], adam_beta1=d["adam_beta1"],
                            adam_beta2=d["adam_beta2"], adam_eps=d["adam_eps"],
                            adam_weight_decay=d["adam_weight_decay"], adam_step=adam_step)
+
+
+def block_rel_max(a, b, bs: int = 256) -> float:
+    """Largest relative Frobenius error over the bs x bs blocks of a unit (the
+    GEMM's output tile size): a single wrong output tile, which moves a large
+    unit's overall error by only ~sqrt(tile / unit), shows here as O(1)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    worst = 0.0
+    for i in range(0, b.shape[0], bs):
+        for j in range(0, b.shape[1], bs):
+            nb = np.linalg.norm(b[i:i + bs, j:j + bs])
+            if nb == 0.0:
+                continue
+            worst = max(worst, float(np.linalg.norm(a[i:i + bs, j:j + bs] - b[i:i + bs, j:j + bs]) / nb))
+    return worst
+
+
+# Per-block bound next to the per-unit 2e-2 of the bf16 path: a block holds
+# a small share of a unit's elements, so its error fluctuates more than the
+# unit's; a tile that is wrong reads O(1).
+BLOCK_TOL_BF16 = 5e-2

@@ -117,12 +117,37 @@ def test_plan_rejects(row, status):
 
 def test_auto_method_resolution():
     _lib_or_skip()
-    # Gram only where n/m > 5/3 and m >= 512; the plan reports the resolved method
+    # Gram only where its fp16 chain is accurate, m >= 512 and n >= 3m; the
+    # plan reports the resolved method
     table = [(0, 1, 4096, 14336, 0, 0), (0, 1, 14336, 4096, 0, 0), (0, 1, 4096, 4096, 0, 0),
-             (0, 1, 1024, 4096, 0, 0), (0, 1, 256, 4096, 0, 0), (0, 1, 600, 1000, 0, 0),
-             (0, 1, 600, 1001, 0, 0)]
+             (0, 1, 1024, 4096, 0, 0), (0, 1, 256, 4096, 0, 0), (0, 1, 600, 1799, 0, 0),
+             (0, 1, 600, 1800, 0, 0), (0, 1, 511, 4096, 0, 0), (0, 1, 512, 1536, 0, 0)]
     got = [b[5] for b in mo.muon_plan_buckets(mo.muon_plan_create(table, mo.MUON_NS_AUTO))]
-    assert got == [1, 1, 0, 1, 0, 0, 1]
+    assert got == [1, 1, 0, 1, 0, 0, 1, 0, 1]
+    # auto never changes the compute dtype
+    assert all(b[4] == 1 for b in mo.muon_plan_buckets(mo.muon_plan_create(table, mo.MUON_NS_AUTO)))
+
+
+def test_explicit_gram_outside_fp16_region_computes_in_fp32():
+    _lib_or_skip()
+    table = [(0, 1, 256, 1024, 0, 0), (0, 1, 768, 768, 0, 0), (0, 1, 768, 3072, 0, 0),
+             (0, 1, 3072, 768, 0, 0), (0, 1, 512, 860, 0, 0), (0, 0, 256, 512, 0, 0)]
+    b = mo.muon_plan_buckets(mo.muon_plan_create(table, mo.MUON_NS_GRAM))
+    assert [x[5] for x in b] == [1] * 6
+    # compute dtype: fp32 (0) outside m >= 512 and n >= 3m, bf16 (1) inside;
+    # an fp32 parameter computes in fp32 anyway
+    assert [x[4] for x in b] == [0, 0, 1, 1, 0, 0]
+    # forcing bf16 compute does not override it
+    b = mo.muon_plan_buckets(mo.muon_plan_create(table, mo.MUON_NS_GRAM, 1))
+    assert [x[4] for x in b] == [0, 0, 1, 1, 0, 0]
+    # the standard method keeps the requested dtype
+    b = mo.muon_plan_buckets(mo.muon_plan_create(table, mo.MUON_NS_STANDARD))
+    assert [x[4] for x in b] == [1, 1, 1, 1, 1, 0]
+    # ns_orthogonalize sizes its workspace for the same choice: fp32 working
+    # copies take twice the bytes of bf16 ones
+    small16 = mo.ns_orthogonalize_workspace_bytes(256, 1024, 1, mo.MUON_NS_STANDARD)
+    small32 = mo.ns_orthogonalize_workspace_bytes(256, 1024, 0, mo.MUON_NS_GRAM)
+    assert mo.ns_orthogonalize_workspace_bytes(256, 1024, 1, mo.MUON_NS_GRAM) == small32 > small16
 
 
 def test_step_validation_before_any_launch():
@@ -153,7 +178,10 @@ def test_step_validation_before_any_launch():
     assert L.muon_step(plan.handle, ptrs, 1, ctypes.byref(bad), 0x10000, ws, None) == -1
     bad = mo.make_hparams(ns_steps=0)
     assert L.muon_step(plan.handle, ptrs, 1, ctypes.byref(bad), 0x10000, ws, None) == -1
-    bad = mo.make_hparams(ns_steps=2, coeffs=[(1.0, float("inf"), 0.0), (1.0, 0.0, 0.0)])
+    # (the binding refuses a non-finite coefficient itself: pass the array raw)
+    bad = mo.make_hparams(ns_steps=2)
+    raw = (ctypes.c_float * 6)(1.0, float("inf"), 0.0, 1.0, 0.0, 0.0)
+    bad.coeffs = ctypes.cast(raw, ctypes.POINTER(ctypes.c_float))
     assert L.muon_step(plan.handle, ptrs, 1, ctypes.byref(bad), 0x10000, ws, None) == -1
     # unknown scale mode, negative or non-finite extra scale
     for bad in (mo.make_hparams(scale_mode=3), mo.make_hparams(extra_scale=-1.0),
@@ -213,3 +241,38 @@ def test_step_binding_checks_buffers():
     for p, g, m in bad_cases:
         with pytest.raises(ValueError):
             mo.muon_step(plan, p, g, m, ea, es, hp, 0x10000)
+
+
+@pytest.mark.parametrize("coeffs,steps", [
+    ([(3.4445, -4.775, 2.0315)] * 3, 5),   # too few rows
+    ([(3.4445, -4.775, 2.0315)] * 6, 5),   # too many rows
+    ([(3.4445, -4.775)] * 5, 5),           # rows of two
+    ([(1.0, float("nan"), 0.0)] * 2, 2),   # non-finite
+])
+def test_binding_rejects_bad_coefficient_tables(coeffs, steps):
+    """A coefficient table must have exactly `steps` rows of three finite
+    numbers (or be a single triple): the library reads 3 * steps floats."""
+    with pytest.raises(ValueError):
+        mo.make_hparams(ns_steps=steps, coeffs=coeffs)
+    import torch
+    with pytest.raises(ValueError):
+        mo.ns_orthogonalize(torch.zeros(4, 8), steps=steps, coeffs=coeffs)
+    # one triple is broadcast to every step
+    hp = mo.make_hparams(ns_steps=steps, coeffs=(3.4445, -4.775, 2.0315))
+    assert [hp.coeffs[i] for i in range(3 * steps)] == pytest.approx([3.4445, -4.775, 2.0315] * steps)
+
+
+def test_binding_rejects_host_tensors():
+    """Tensors in host memory never reach the library as device pointers:
+    the binding raises before any call (no GPU is touched)."""
+    _lib_or_skip()
+    import torch
+    X = torch.zeros(64, 96, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device memory"):
+        mo.ns_orthogonalize(X)
+    plan = mo.muon_plan_create([(0, 1, 4, 8, 0, 0)])
+    hp = mo.make_hparams()
+    p = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device memory"):
+        mo.muon_step(plan, [p], [p.clone()], [torch.zeros(4, 8)], [None], [None], hp,
+                     torch.empty(mo.muon_plan_workspace_bytes(plan), dtype=torch.uint8))

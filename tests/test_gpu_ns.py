@@ -1,16 +1,18 @@
 """GPU parity of ns_orthogonalize (the Newton-Schulz chain alone) against
-the fp64 oracle, plus the bit-exact symmetries of the HIP path.
+the plain C++ fp64 reference (oracle/muon_ref.cpp), plus the bit-exact
+symmetries of the HIP path.
 
-Tolerances (relative Frobenius error against the oracle): 2e-2 on the bf16
-path, 1e-4 on the fp32 path.  Inputs are the workload generator's low-rank
-gradients (geometric spectrum 1..1e-3, 1e-3 noise), rounded once to the
-storage dtype; the oracle receives exactly those values."""
+Tolerances (relative Frobenius error against the reference): 2e-2 on the
+bf16 path, 1e-4 on the fp32 path.  Inputs are the workload generator's
+low-rank gradients (geometric spectrum 1..1e-3, 1e-3 noise), or
+well-conditioned matrices for the shapes below 64 on a side, rounded once to
+the storage dtype; the reference receives exactly those values."""
 import numpy as np
 import pytest
 import torch
 
-import oracle
-from tests.gpu_util import dev, f64, rel
+from oracle import cref
+from tests.gpu_util import BLOCK_TOL_BF16, block_rel_max, dev, f64, rel
 from workloads import gen
 
 mo = pytest.importorskip("matrix_orthogonalizing_optimizer_amd")
@@ -35,12 +37,8 @@ def _run(G, method=0, steps=5, coeffs=None):
 # several tiles plus ragged tails, tall and wide, the workload unit shapes
 SHAPES = [(256, 512), (512, 256), (300, 700), (700, 300), (129, 1000), (768, 768), (128, 2048),
           (1408, 2048), (2048, 1408)]
-# tiny and degenerate shapes: the fp32 path pins the tiling logic exactly.
-# On the bf16 path such shapes are not held to 2e-2: with min(m, n) < 64 the
-# workload generator leaves normalized singular values below the band
-# threshold (~1.6e-3), where five quintic steps amplify the per-step bf16
-# rounding by up to a^5 ~ 485 (the tiny-shape misses observed are 2.1-3.2e-2).
-TINY = [(37, 50), (50, 37), (1, 64), (64, 1), (8, 8), (1, 1), (3, 200)]
+# tiny and degenerate shapes (one 128 x 128 tile, mostly padding)
+TINY = [(37, 50), (50, 37), (1, 64), (64, 1), (8, 8), (1, 1), (3, 200), (63, 63), (64, 200)]
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -49,31 +47,57 @@ def test_standard_matches_oracle(shape, dtype):
     print(f"ns standard {shape} {dtype}", flush=True)
     G = _input(*shape, dtype, seed=shape[0] * 7919 + shape[1])
     O = f64(_run(G))
-    ref = oracle.orthogonalize(f64(G))
+    ref = cref.orthogonalize(f64(G))
     assert rel(O, ref) <= TOL[dtype], rel(O, ref)
+    if dtype == torch.bfloat16:
+        assert block_rel_max(O, ref) <= BLOCK_TOL_BF16
 
 
 @pytest.mark.parametrize("shape", TINY)
 def test_standard_tiny_fp32(shape):
-    print(f"ns standard tiny {shape}", flush=True)
+    print(f"ns standard tiny fp32 {shape}", flush=True)
     G = _input(*shape, torch.float32, seed=shape[0] * 7919 + shape[1])
     O = f64(_run(G))
-    ref = oracle.orthogonalize(f64(G))
+    ref = cref.orthogonalize(f64(G))
     assert rel(O, ref) <= 1e-4, rel(O, ref)
 
 
-# The Gram rewrite is meant for wide matrices (aspect >= 3.5 here, as in the
-# 4096 x 14336 workload).  It amplifies rounding in R's small eigenvalues by up
-# to a^2 per step, so its fp16 error falls with m: ~1.0e-2 at m = 512 and
-# ~0.5e-2 at m = 1024 (emulated and measured), above 2e-2 only for m <~ 300.
+@pytest.mark.parametrize("shape", TINY)
+def test_standard_tiny_bf16_well_conditioned(shape):
+    """The bf16 path on shapes below 64 on a side, two Newton-Schulz steps
+    (every kernel of the chain, both working copies of the iteration).  The
+    workload generator is not used here: at these sizes it leaves normalized
+    singular values below ~1.6e-3, where the quintic amplifies any rounding
+    by up to a^5 ~ 485.  Singular values uniform in [0.3, 1] avoid that, but
+    with normalized values near 1/sqrt(m) three or more steps pass through
+    the band where the map expands errors, and a rounding emulation of bf16
+    storage gives 1.3-3e-2 after five steps on some of these shapes: a
+    property of the iteration in 16-bit arithmetic, not of the tiles.  After
+    two steps the emulation stays below 1.3e-2."""
+    print(f"ns standard tiny bf16 {shape}", flush=True)
+    G = gen.conditioned_matrix(*shape, 0.3, 1.0, seed=shape[0] * 131 + shape[1]).to(torch.bfloat16)
+    O = f64(_run(G, steps=2))
+    ref = cref.orthogonalize(f64(G), steps=2)
+    assert rel(O, ref) <= 2e-2, rel(O, ref)
+
+
+# Gram variant.  Inside m >= 512, n >= 3m the chain runs in fp16 (R scaled by
+# a power of two); every other Gram shape computes in fp32, so an explicit
+# request for the Gram variant is held to the same tolerance everywhere.
+GRAM_SHAPES = [(512, 1792), (1792, 512), (1024, 3584), (1000, 3500),       # fp16 chain
+               (256, 1024), (300, 1100), (768, 768), (512, 860), (96, 300)]  # fp32
+GRAM_WIDE_FP16 = [(768, 3072), (3072, 768)]
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("shape", [(512, 1792), (1792, 512), (1024, 3584), (1000, 3500)])
+@pytest.mark.parametrize("shape", GRAM_SHAPES + GRAM_WIDE_FP16)
 def test_gram_matches_oracle(shape, dtype):
     print(f"ns gram {shape} {dtype}", flush=True)
-    G = _input(*shape, dtype, seed=shape[0] * 31 + shape[1], rank=64)
-    O = f64(_run(G, method=1))
-    ref = oracle.orthogonalize(f64(G), method="standard")
-    assert rel(O, ref) <= TOL[dtype], rel(O, ref)
+    for rank in (8, 64):
+        G = _input(*shape, dtype, seed=shape[0] * 31 + shape[1] + rank, rank=rank)
+        O = f64(_run(G, method=1))
+        ref = cref.orthogonalize(f64(G), method="standard")
+        assert rel(O, ref) <= TOL[dtype], (rank, rel(O, ref))
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -81,27 +105,22 @@ def test_coefficient_schedule_and_steps(dtype):
     G = _input(200, 330, dtype, seed=5)
     sched = [(3.4445, -4.7750, 2.0315)] * 3 + [(1.5, -0.5, 0.0)] * 3
     O = f64(_run(G, steps=6, coeffs=sched))
-    ref = oracle.orthogonalize(f64(G), steps=6, coeffs=sched)
+    ref = cref.orthogonalize(f64(G), steps=6, coeffs=sched)
     assert rel(O, ref) <= TOL[dtype]
     O1 = f64(_run(G, steps=1))
-    assert rel(O1, oracle.orthogonalize(f64(G), steps=1)) <= TOL[dtype]
+    assert rel(O1, cref.orthogonalize(f64(G), steps=1)) <= TOL[dtype]
 
 
-def test_zero_and_sign_and_transpose_bit_exact():
+def test_zero_transpose_and_scaling_bit_exact():
     d = dev()
     Z = torch.zeros(64, 96, dtype=torch.bfloat16, device=d)
     mo.ns_orthogonalize(Z)
     assert torch.count_nonzero(Z).item() == 0
     G = _input(300, 700, torch.bfloat16, seed=11)
     a = _run(G)
-    b = _run(-G)
     c = _run(G.t().contiguous())
-    torch.cuda.synchronize()
     # implicit transposition of a tall matrix: the identical chain runs
     assert torch.equal(c, a.t())
-    # NS(-G) = -NS(G) holds up to rounding only: the MFMA accumulate is not
-    # sign-symmetric bit for bit
-    assert rel(f64(b), -f64(a)) <= 1e-2
     # power-of-two scaling leaves the result unchanged
     assert torch.equal(_run(G * 4), a)
 
@@ -121,5 +140,5 @@ def test_strided_rows_in_place():
     view = big[:, :160]
     mo.ns_orthogonalize(view)
     torch.cuda.synchronize()
-    assert rel(f64(view), oracle.orthogonalize(f64(G))) <= 1e-4
+    assert rel(f64(view), cref.orthogonalize(f64(G))) <= 1e-4
     assert torch.count_nonzero(big[:, 160:]).item() == 0

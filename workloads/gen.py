@@ -57,6 +57,20 @@ def lowrank_gradient(rows: int, cols: int, rank: int, seed: int, device="cpu",
     return G.to(dtype)
 
 
+def conditioned_matrix(rows: int, cols: int, smin: float, smax: float, seed: int, device="cpu",
+                       dtype=torch.float32) -> torch.Tensor:
+    """U diag(s) V^T with U, V random orthonormal (QR of Gaussian matrices)
+    and the min(rows, cols) singular values s uniform in [smin, smax]: a
+    well-conditioned input whose normalized singular values all stay clear of
+    the range the quintic amplifies.  Computed in fp64 on the CPU."""
+    g = _gen("cpu", seed)
+    k = min(rows, cols)
+    U, _ = torch.linalg.qr(torch.randn(rows, k, generator=g, dtype=torch.float64))
+    V, _ = torch.linalg.qr(torch.randn(cols, k, generator=g, dtype=torch.float64))
+    s = smin + (smax - smin) * torch.rand(k, generator=g, dtype=torch.float64)
+    return ((U * s) @ V.T).to(device=device, dtype=dtype)
+
+
 def normal(rows: int, cols: int, std: float, seed: int, device="cpu", dtype=torch.float32):
     g = _gen(device, seed)
     wdt = torch.float64 if str(device) == "cpu" else torch.float32
