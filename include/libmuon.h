@@ -54,14 +54,17 @@ typedef enum {
  * m x n unit, or the Gram variant, which iterates on the square R = X X^T
  * (m = min, n = max of the unit's sides).  The Gram chain runs in fp16 with
  * R scaled by a power of two only where that stays within the bf16
- * tolerance on the workload gradients, m >= 512 and n >= 3m; a Gram unit
- * outside that region with a 16-bit compute dtype computes in fp32 instead
- * (its bucket reports compute dtype MUON_F32), so MUON_NS_GRAM never trades
- * accuracy for speed silently.  MUON_NS_AUTO picks Gram exactly in that
- * region, where it also does less work (executed cost with symmetric
- * products: standard steps (3 m^2 n + m^3), Gram 3 m^2 n + (6 steps - 5)
- * m^3, so Gram is cheaper for n/m > 5/3), and the standard method
- * elsewhere.  Plans report the method and compute dtype of every bucket. */
+ * tolerance on the workload gradients, m >= 512 and n >= 3m.  An explicit
+ * MUON_NS_GRAM outside that region is served in a precision that meets the
+ * tolerance of the requested compute dtype: with bf16 the Gram chain runs
+ * in fp32 (the bucket reports compute dtype MUON_F32); with fp32 the unit
+ * runs the standard iteration (the bucket reports MUON_NS_STANDARD), since
+ * an fp32 Gram chain there exceeds the fp32 tolerance.  MUON_NS_AUTO picks
+ * Gram exactly inside the region, where it also does less work (executed
+ * cost with symmetric products: standard steps (3 m^2 n + m^3), Gram
+ * 3 m^2 n + (6 steps - 5) m^3, so Gram is cheaper for n/m > 5/3), and the
+ * standard method elsewhere.  Plans report the method and compute dtype of
+ * every bucket. */
 typedef enum { MUON_NS_STANDARD = 0, MUON_NS_GRAM = 1, MUON_NS_AUTO = 2 } muon_ns_method;
 
 /* Storage dtype of parameters and gradients.  Momentum and AdamW moments are
@@ -242,7 +245,7 @@ muon_status muon_step(const muon_plan* plan, const muon_param_ptrs* ptrs, int32_
  * in place: X <- NS_steps(X / ||X||_F) ([Blog] "Newton-Schulz Iteration":
  * X <- a_k X + (b_k A + c_k A^2) X with A = X X^T), a tall X being processed
  * as its transpose ([Blog] "Sign of a Matrix"); method standard, Gram
- * ([DeepSpeed]; fp32 outside the fp16 region described above) or auto.
+ * ([DeepSpeed]; resolved as described above) or auto.
  * coeffs: host array of steps x 3 floats as in muon_hparams, or NULL.  A
  * zero matrix stays zero.  workspace: device memory of at least
  * ns_orthogonalize_workspace_bytes bytes, owned by the caller, contents
@@ -256,6 +259,7 @@ muon_status ns_orthogonalize(void* X, int64_t rows, int64_t cols, int64_t ld, in
                              void* workspace, size_t workspace_bytes, void* stream);
 muon_status ns_orthogonalize_workspace_bytes(int64_t rows, int64_t cols, int32_t dtype,
                                              int32_t method, size_t* bytes);
+
 
 /* Optional per-kernel timing, for benchmarks.  While enabled (process-wide),
  * every kernel launch of the library is bracketed by two HIP events recorded

@@ -277,14 +277,20 @@ double unit_scale(const muon_hparams& hp, const PlanUnit& u) {
   }
 }
 
-muon_status coeff_table(int32_t steps, const float* coeffs, std::vector<float>& out) {
+// Per-step (a, b, c), held by value (no heap use on the paths that must not
+// allocate).
+struct CoeffTable {
+  float v[3 * MAX_NS_STEPS];
+  const float* data() const { return v; }
+};
+
+muon_status coeff_table(int32_t steps, const float* coeffs, CoeffTable& out) {
   if (steps < 1 || steps > MAX_NS_STEPS) return MUON_E_ARG;
-  out.resize((size_t)steps * 3);
   for (int k = 0; k < steps; ++k)
     for (int j = 0; j < 3; ++j) {
       const float v = coeffs ? coeffs[3 * k + j] : kQuintic[j];
       if (!finite(v)) return MUON_E_ARG;
-      out[(size_t)3 * k + j] = v;
+      out.v[3 * k + j] = v;
     }
   return MUON_OK;
 }
@@ -388,7 +394,7 @@ muon_status muon_step(const muon_plan* plan, const muon_param_ptrs* ptrs, int32_
   const PlanImpl& P = plan->impl;
   if (n != (int32_t)P.table.size()) return MUON_E_PLAN;
   if (n > 0 && !ptrs) return MUON_E_ARG;
-  std::vector<float> coeffs;
+  CoeffTable coeffs;
   muon_status st = coeff_table(hp->ns_steps, hp->coeffs, coeffs);
   if (st != MUON_OK) return st;
   if (!finite(hp->lr) || !finite(hp->momentum) || !finite(hp->weight_decay) || !finite(hp->rms_scale))
@@ -534,7 +540,7 @@ static muon_status ns_bucket(int64_t rows, int64_t cols, int32_t dtype, int32_t 
   b.n = (int32_t)std::max(rows, cols);
   b.tall = rows > cols ? 1 : 0;
   b.pdtype = dtype;
-  b.method = resolve_method(method, b.m, b.n);
+  b.method = resolve_method(method, dtype, b.m, b.n);
   b.cdtype = resolve_cdtype(dtype, b.method, b.m, b.n);
   b.first = 0;
   b.count = 1;
@@ -565,7 +571,7 @@ muon_status ns_orthogonalize(void* X, int64_t rows, int64_t cols, int64_t ld, in
   PlanBucket b;
   muon_status st = ns_bucket(rows, cols, dtype, method, b);
   if (st != MUON_OK) return st;
-  std::vector<float> cf;
+  CoeffTable cf;
   st = coeff_table(steps, coeffs, cf);
   if (st != MUON_OK) return st;
   if (ld < cols) return MUON_E_SHAPE;

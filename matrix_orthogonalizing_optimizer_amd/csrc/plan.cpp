@@ -26,13 +26,19 @@ static size_t align_ws(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALI
 // to square, or smaller, the normalized noise spectrum reaches down to where
 // the quintic amplifies the chain's rounding (emulated: 5.3e-2 at 512 x 860,
 // 5.8e-2 at 768 x 768, 3.5e-2 at 256 x 512; at most 1.25e-2 inside the
-// region).  Where it also does less work than the standard method (n/m > 5/3),
-// MUON_NS_AUTO picks Gram.
+// region).  MUON_NS_AUTO picks Gram exactly there (where it also does less
+// work than the standard method, n/m > 5/3).  An explicit Gram request
+// outside the region is served in a precision that meets the tolerance: a
+// 16-bit compute dtype runs the Gram chain in fp32 (~1e-4, far inside the
+// bf16 tolerance); an fp32 one runs the standard iteration, since the fp32
+// Gram chain loses ~50x against it there (1.1-1.8e-4 measured on 768 x 768,
+// 512 x 860 and 96 x 300, above the fp32 tolerance of 1e-4).
 bool gram_fp16_ok(int64_t m, int64_t n) { return m >= 512 && n >= 3 * m; }
 
-int32_t resolve_method(int32_t method, int64_t m, int64_t n) {
-  if (method != MUON_NS_AUTO) return method;
-  return gram_fp16_ok(m, n) ? MUON_NS_GRAM : MUON_NS_STANDARD;
+int32_t resolve_method(int32_t method, int32_t cdtype, int64_t m, int64_t n) {
+  if (method == MUON_NS_AUTO) return gram_fp16_ok(m, n) ? MUON_NS_GRAM : MUON_NS_STANDARD;
+  if (method == MUON_NS_GRAM && cdtype == MUON_F32 && !gram_fp16_ok(m, n)) return MUON_NS_STANDARD;
+  return method;
 }
 
 int32_t resolve_cdtype(int32_t cdtype, int32_t method, int64_t m, int64_t n) {
@@ -130,8 +136,9 @@ muon_status build_plan(const muon_param_shape* table, int32_t n, const muon_plan
     const PlanUnit& u = order[i];
     const int32_t m = (int32_t)std::min(u.rows, u.cols), nn = (int32_t)std::max(u.rows, u.cols);
     const int32_t pdt = P.table[u.param].dtype;
-    const int32_t meth = resolve_method(o.ns_method, m, nn);
-    const int32_t cdt = resolve_cdtype(o.ns_dtype < 0 ? pdt : o.ns_dtype, meth, m, nn);
+    const int32_t req = o.ns_dtype < 0 ? pdt : o.ns_dtype;
+    const int32_t meth = resolve_method(o.ns_method, req, m, nn);
+    const int32_t cdt = resolve_cdtype(req, meth, m, nn);
     size_t bi = 0;
     for (; bi < P.buckets.size(); ++bi) {
       const PlanBucket& b = P.buckets[bi];

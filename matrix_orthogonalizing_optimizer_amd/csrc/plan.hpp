@@ -52,9 +52,12 @@ int64_t round_up(int64_t x, int64_t m);
 int32_t elem_size(int32_t cdtype);
 void bucket_derive(PlanBucket& b, size_t chunk_cap_bytes);
 bool bucket_addressable(const PlanBucket& b);  // one unit's n x m operand < 2^31 bytes
-int32_t resolve_method(int32_t method, int64_t m, int64_t n);  // MUON_NS_AUTO -> standard or Gram
 bool gram_fp16_ok(int64_t m, int64_t n);  // the fp16 Gram chain meets the bf16 tolerance
-int32_t resolve_cdtype(int32_t cdtype, int32_t method, int64_t m, int64_t n);  // Gram outside it: fp32
+// the method a unit runs (AUTO -> standard or Gram; an fp32 Gram request
+// outside gram_fp16_ok -> standard), cdtype the requested compute dtype
+int32_t resolve_method(int32_t method, int32_t cdtype, int64_t m, int64_t n);
+// the compute dtype it runs in (a bf16 Gram unit outside gram_fp16_ok -> fp32)
+int32_t resolve_cdtype(int32_t cdtype, int32_t method, int64_t m, int64_t n);
 size_t per_unit_data_bytes(const PlanBucket& b);
 
 muon_status build_plan(const muon_param_shape* table, int32_t n, const muon_plan_options* opts,

@@ -263,11 +263,16 @@ int64_t ref_plan(const int64_t* table, int32_t n, int32_t method, int32_t ns_dty
     const int64_t pdt = table[6 * u.p + 1];
     const int64_t m = std::min(u.rows, u.cols), nn = std::max(u.rows, u.cols);
     // Gram's fp16 chain is within the bf16 tolerance only for m >= 512 and
-    // n >= 3m: method 2 picks Gram there (where it also does less work), and
-    // a Gram unit outside it computes in fp32 (dtype code 0)
+    // n >= 3m: method 2 picks Gram there (where it also does less work).
+    // An explicit Gram request outside it runs its chain in fp32 when the
+    // requested compute dtype is bf16 (code 1 -> 0), and runs the standard
+    // method when it is fp32 (the fp32 chain there is above the fp32
+    // tolerance)
     const bool fp16_ok = m >= 512 && nn >= 3 * m;
-    const int64_t meth = method == 2 ? (fp16_ok ? 1 : 0) : method;
     int64_t cdt = ns_dtype < 0 ? pdt : ns_dtype;
+    int64_t meth = method;
+    if (method == 2) meth = fp16_ok ? 1 : 0;
+    else if (method == 1 && cdt == 0 && !fp16_ok) meth = 0;
     if (meth == 1 && cdt == 1 && !fp16_ok) cdt = 0;
     const std::vector<int64_t> key = {m, nn, u.tall, pdt, cdt, meth};
     size_t b = 0;

@@ -287,21 +287,26 @@ def gram_fp16_ok(m: int, n: int) -> bool:
     return m >= 512 and n >= 3 * m
 
 
-def resolve_method(method: int, m: int, n: int) -> int:
+def resolve_method(method: int, dt: int, m: int, n: int) -> int:
     """Method 2 ("auto") picks, per unit, the Gram variant where its fp16
     chain is accurate (``gram_fp16_ok``), which also lies where it executes
     less work than the standard method (standard: steps (3 m^2 n + m^3) with
     symmetric products, Gram: 3 m^2 n + (6 steps - 5) m^3, i.e. n/m > 5/3);
-    the standard method otherwise."""
-    if method != 2:
-        return method
-    return 1 if gram_fp16_ok(m, n) else 0
+    the standard method otherwise.  An explicit Gram request (1) for the
+    fp32 compute dtype (code 0) outside that region is served by the
+    standard method: the fp32 Gram chain there measured above the fp32
+    tolerance (1.1-1.8e-4 on 768 x 768, 512 x 860, 96 x 300)."""
+    if method == 2:
+        return 1 if gram_fp16_ok(m, n) else 0
+    if method == 1 and dt == DT_F32 and not gram_fp16_ok(m, n):
+        return 0
+    return method
 
 
 def resolve_compute_dtype(dt: int, method: int, m: int, n: int) -> int:
-    """A Gram unit outside ``gram_fp16_ok`` computes in fp32 (code 0) instead
-    of bf16 (code 1), so that an explicit request for the Gram variant never
-    leaves the tolerance."""
+    """A bf16 (code 1) Gram unit outside ``gram_fp16_ok`` computes in fp32
+    (code 0), so that an explicit request for the Gram variant never leaves
+    the tolerance."""
     if method == 1 and dt == DT_BF16 and not gram_fp16_ok(m, n):
         return DT_F32
     return dt
@@ -318,8 +323,9 @@ def plan_buckets(table, method: int, ns_dtype: int = -1):
     members = []
     for ui, u in enumerate(units):
         pdt = table[u.param][1]
-        meth = resolve_method(method, u.m, u.n)
-        dt = resolve_compute_dtype(pdt if ns_dtype < 0 else ns_dtype, meth, u.m, u.n)
+        req = pdt if ns_dtype < 0 else ns_dtype
+        meth = resolve_method(method, req, u.m, u.n)
+        dt = resolve_compute_dtype(req, meth, u.m, u.n)
         key = (u.m, u.n, 1 if u.tall else 0, pdt, dt, meth)
         found = -1
         for bi, k in enumerate(keys):

@@ -128,26 +128,37 @@ def test_auto_method_resolution():
     assert all(b[4] == 1 for b in mo.muon_plan_buckets(mo.muon_plan_create(table, mo.MUON_NS_AUTO)))
 
 
-def test_explicit_gram_outside_fp16_region_computes_in_fp32():
+def test_explicit_gram_outside_fp16_region():
+    """An explicit Gram request outside m >= 512, n >= 3m: a bf16 unit runs
+    the Gram chain in fp32 (compute dtype 0), an fp32 unit the standard
+    method; inside the region Gram runs in the requested dtype."""
     _lib_or_skip()
     table = [(0, 1, 256, 1024, 0, 0), (0, 1, 768, 768, 0, 0), (0, 1, 768, 3072, 0, 0),
-             (0, 1, 3072, 768, 0, 0), (0, 1, 512, 860, 0, 0), (0, 0, 256, 512, 0, 0)]
+             (0, 1, 3072, 768, 0, 0), (0, 1, 512, 860, 0, 0), (0, 0, 256, 512, 0, 0),
+             (0, 0, 512, 1536, 0, 0)]
+    meth = lambda b: [x[5] for x in b]
+    cdt = lambda b: [x[4] for x in b]
     b = mo.muon_plan_buckets(mo.muon_plan_create(table, mo.MUON_NS_GRAM))
-    assert [x[5] for x in b] == [1] * 6
-    # compute dtype: fp32 (0) outside m >= 512 and n >= 3m, bf16 (1) inside;
-    # an fp32 parameter computes in fp32 anyway
-    assert [x[4] for x in b] == [0, 0, 1, 1, 0, 0]
-    # forcing bf16 compute does not override it
+    assert meth(b) == [1, 1, 1, 1, 1, 0, 1]
+    assert cdt(b) == [0, 0, 1, 1, 0, 0, 0]
+    # compute forced to bf16: every unit runs Gram, outside the region in fp32
     b = mo.muon_plan_buckets(mo.muon_plan_create(table, mo.MUON_NS_GRAM, 1))
-    assert [x[4] for x in b] == [0, 0, 1, 1, 0, 0]
+    assert meth(b) == [1] * 7
+    assert cdt(b) == [0, 0, 1, 1, 0, 0, 1]
+    # compute forced to fp32: Gram only inside the region
+    b = mo.muon_plan_buckets(mo.muon_plan_create(table, mo.MUON_NS_GRAM, 0))
+    assert meth(b) == [0, 0, 1, 1, 0, 0, 1]
+    assert cdt(b) == [0] * 7
     # the standard method keeps the requested dtype
     b = mo.muon_plan_buckets(mo.muon_plan_create(table, mo.MUON_NS_STANDARD))
-    assert [x[4] for x in b] == [1, 1, 1, 1, 1, 0]
-    # ns_orthogonalize sizes its workspace for the same choice: fp32 working
-    # copies take twice the bytes of bf16 ones
-    small16 = mo.ns_orthogonalize_workspace_bytes(256, 1024, 1, mo.MUON_NS_STANDARD)
-    small32 = mo.ns_orthogonalize_workspace_bytes(256, 1024, 0, mo.MUON_NS_GRAM)
-    assert mo.ns_orthogonalize_workspace_bytes(256, 1024, 1, mo.MUON_NS_GRAM) == small32 > small16
+    assert meth(b) == [0] * 7 and cdt(b) == [1, 1, 1, 1, 1, 0, 0]
+    # ns_orthogonalize sizes its workspace for the same resolution: an fp32
+    # Gram request outside the region takes the standard method's workspace,
+    # a bf16 one fp32 working copies (more than its standard workspace)
+    assert (mo.ns_orthogonalize_workspace_bytes(256, 1024, 0, mo.MUON_NS_GRAM)
+            == mo.ns_orthogonalize_workspace_bytes(256, 1024, 0, mo.MUON_NS_STANDARD))
+    assert (mo.ns_orthogonalize_workspace_bytes(256, 1024, 1, mo.MUON_NS_GRAM)
+            > mo.ns_orthogonalize_workspace_bytes(256, 1024, 1, mo.MUON_NS_STANDARD))
 
 
 def test_step_validation_before_any_launch():

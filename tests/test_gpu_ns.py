@@ -142,3 +142,31 @@ def test_strided_rows_in_place():
     torch.cuda.synchronize()
     assert rel(f64(view), cref.orthogonalize(f64(G))) <= 1e-4
     assert torch.count_nonzero(big[:, 160:]).item() == 0
+
+
+def _ulp_bf16(x):
+    return np.exp2(np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126))) - 7)
+
+
+@pytest.mark.parametrize("shape", [(300, 700), (256, 512), (1024, 1024)])
+def test_sign_symmetry(shape):
+    """NS(-G) = -NS(G).  With -G every product of the chain sees negated
+    operands only in the update products (A = X X^T and P are identical).
+    fp32 path: bit-exact after five steps (the fp32 matrix instruction
+    accumulates sign-symmetrically).  bf16 path: after one step (one product
+    of each kind) at most 1e-4 of the elements differ, each by at most one
+    bf16 ulp of its value: the bf16 matrix instruction's accumulation is not
+    sign-symmetric bit for bit (measured: 0 of 210000 and 131072, 8 of
+    1048576 elements).  After five steps those single-ulp differences have
+    been carried through four more steps like any rounding: the bound is
+    1e-2 relative (measured 0.5-4.8e-3)."""
+    print(f"ns sign symmetry {shape}", flush=True)
+    G32 = _input(*shape, torch.float32, seed=11)
+    assert torch.equal(_run(-G32), -_run(G32))
+    G = G32.to(torch.bfloat16)
+    a, b = f64(_run(G, steps=1)), f64(_run(-G, steps=1))
+    diff = np.abs(a + b)
+    assert np.count_nonzero(diff) <= 1e-4 * a.size, np.count_nonzero(diff)
+    assert np.all(diff <= _ulp_bf16(a))
+    a, b = f64(_run(G)), f64(_run(-G))
+    assert rel(b, -a) <= 1e-2, rel(b, -a)
