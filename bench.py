@@ -39,8 +39,6 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--ns-method", choices=["standard", "gram", "auto"], default=None,
                    help="override the workload's Newton-Schulz method")
-    p.add_argument("--cpu-sample", default=",".join(["1024x4096"] * 8),
-                   help="unit shapes the oracle is timed on")
     p.add_argument("--no-probes", action="store_true",
                    help="skip the measured MFMA and copy ceilings")
     p.add_argument("--copy-calibration", action="store_true",
@@ -112,8 +110,12 @@ def main():
     mo.muon_timing_collect()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    host_s = 0.0
     for _ in range(args.steps):
+        h0 = time.perf_counter()
         mo.muon_step(plan, params, grads, moms, eas, ess, hp, ws, stream=stream)
+        host_s += time.perf_counter() - h0
+    t_enqueued = time.perf_counter()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     mo.muon_timing_enable(False)
@@ -133,7 +135,10 @@ def main():
         e = {"launches": r["launches"] // args.steps, "ms_per_step": r["total_ms"] / args.steps,
              "avg_launch_ms": avg}
         if r["flops"] > 0:
-            e["tflops"] = r["flops"] / (r["total_ms"] * 1e-3) / 1e12
+            # the symmetric products compute only upper-triangle tiles: their
+            # dense-equivalent rate is nominal, executed_tflops is what ran
+            key = "nominal_tflops" if name in SYMMETRIC_FAMILIES else "tflops"
+            e[key] = r["flops"] / (r["total_ms"] * 1e-3) / 1e12
         if name in exe:
             e["executed_tflops"] = exe[name] * args.steps / (r["total_ms"] * 1e-3) / 1e12
         if r["bytes"] > 0:
@@ -158,8 +163,13 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.cpu_sample, wl, table)
+        cpu = cpu_baseline(wl, table, "gram" if method == 1 else "standard")
 
+    # muon_step only enqueues: its host time per call against the GPU's time
+    # per step (the host had queued all K steps after this long)
+    host = {"host_ms_per_call": 1e3 * host_s / args.steps,
+            "all_steps_enqueued_after_ms": 1e3 * (t_enqueued - t_start),
+            "gpu_ms_for_all_steps": 1e3 * elapsed}
     n_units = len(mo.muon_plan_units(plan))
     adam_elems = sum(r[2] * r[3] for r in table if r[0] == 1)
     muon_elems = sum(r[2] * r[3] for r in table if r[0] == 0)
@@ -187,9 +197,13 @@ def main():
                    "ns_executed_tflop_per_step": exe_total / 1e12},
         "roofline": roofline,
         "kernels": kernels,
+        "enqueue": host,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+SYMMETRIC_FAMILIES = ("ns_gram_A", "ns_poly_P", "gram_r0", "gram_p", "gram_q", "gram_t", "gram_r")
 
 
 def executed_flops(buckets, steps):
@@ -302,55 +316,98 @@ def measured_traffic(workload: str):
     return float(vals["traffic_bytes_per_launch"])
 
 
-def cpu_baseline(sample: str, wl, table):
-    """The fp64 oracle as it stands, timed on this host on a bounded sample:
-    one full Muon unit update (momentum, Newton-Schulz, scaled update) per
-    listed unit shape, with the workload's gradient generator.  The plain C++
-    reference (std::thread over all host cores) is the baseline; the numpy
-    reference (BLAS matmul) is timed beside it for context.  Reported as
-    nominal Newton-Schulz TFLOP/s, the metric's unit."""
+SMALL_WORKLOADS = ("single_256x512_fp32", "gpt2_small_bf16")
+CPU_SAMPLE_MAX_M = 1024   # largest m of a scaled-down per-bucket sample unit
+ADAMW_CHUNK = 1 << 24     # AdamW elements per reference call
+
+
+def cpu_baseline(wl, table, method: str):
+    """The plain C++ fp64 reference (oracle/muon_ref.cpp, std::thread over
+    every host core it sees; not tuned for this) timed on this host.
+
+    The 256x512 and GPT-2-small-shaped workloads are timed in full: one whole
+    step over the table (momentum, Newton-Schulz, scaled update for every
+    unit; AdamW for every other element).  For the large workloads one unit
+    per shape bucket is timed, at its real shape when m <= 1024 and otherwise
+    at the same aspect ratio scaled down by the smallest power of two that
+    brings m to 1024 or less; its time is scaled up by the ratio of nominal
+    Newton-Schulz FLOPs (full unit / sample) and by the bucket's unit count.
+    AdamW is timed on every element (in chunks of 2^24 elements).  Reported
+    in the metric's unit (nominal NS TFLOP/s) and as ms per step."""
     import numpy as np
     import torch
 
-    import oracle
     from oracle import cref
     from workloads import configs, gen
 
     hp = wl.hp
-    shapes = [tuple(int(x) for x in s.split("x")) for s in sample.split(",")]
-    grads = [gen.lowrank_gradient(r, c, wl.rank, 99 + i, "cpu", torch.float64).to(torch.bfloat16).double().numpy()
-             for i, (r, c) in enumerate(shapes)]
-    flops = sum(hp["ns_steps"] * (4.0 * min(r, c) ** 2 * max(r, c) + 2.0 * min(r, c) ** 3) for r, c in shapes)
+    ohp = _cref_hparams(hp)
+    threads = cref.threads()
     step_flops = hp["ns_steps"] * configs.ns_flops(table)
+    if wl.name in SMALL_WORKLOADS:
+        P, M, EA, ES = gen.make_state(wl, "cpu")
+        G = gen.make_grads(wl, 0, "cpu")
+        f = lambda xs: [None if x is None else x.double().numpy() for x in xs]
+        P, M, EA, ES, G = f(P), f(M), f(EA), f(ES), f(G)
+        t = time.perf_counter()
+        cref.muon_step(table, P, G, M, EA, ES, ohp, method=method)
+        secs = time.perf_counter() - t
+        return {"value": step_flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+                "sample": f"whole step over the full {wl.name} table in the plain C++ fp64 reference "
+                          f"({secs:.1f} s)",
+                "ms_per_step": 1e3 * secs, "extrapolated": False}
+    # large workloads: one (scaled) unit per bucket, AdamW in full
+    buckets = {}
+    for kind, _dt, rows, cols, split, _sd in table:
+        if kind != 0 or rows == 0 or cols == 0:
+            continue
+        h = split if split > 0 else rows
+        key = (h, cols)
+        buckets[key] = buckets.get(key, 0) + rows // h
+    total = 0.0
+    parts = []
+    for i, ((r, c), count) in enumerate(buckets.items()):
+        sc = 1
+        while min(r, c) // sc > CPU_SAMPLE_MAX_M:
+            sc *= 2
+        rs, cs = r // sc, c // sc
+        G = gen.lowrank_gradient(rs, cs, wl.rank, 99 + i, "cpu", torch.float64).to(torch.bfloat16).double().numpy()
+        t = time.perf_counter()
+        cref.muon_step([(0, 1, rs, cs, 0, 0)], [np.zeros((rs, cs))], [G], [np.zeros((rs, cs))], [None], [None],
+                       ohp, method=method)
+        secs = time.perf_counter() - t
+        ns = lambda a, b: 4.0 * min(a, b) ** 2 * max(a, b) + 2.0 * min(a, b) ** 3
+        est = secs * ns(r, c) / ns(rs, cs) * count
+        total += est
+        parts.append(f"{count} x {r}x{c} from {rs}x{cs} ({secs:.1f} s)")
+    adam = sum(r[2] * r[3] for r in table if r[0] == 1)
+    adam_secs = 0.0
+    if adam:
+        n = min(adam, ADAMW_CHUNK)
+        rng = np.random.default_rng(0)
+        w = rng.standard_normal(n) * 0.02
+        g = rng.standard_normal(n) * 1e-3
+        z = np.zeros(n)
+        t = time.perf_counter()
+        done = 0
+        while done < adam:
+            k = min(n, adam - done)
+            cref.adamw(w[:k], g[:k], z[:k], z[:k], 1, hp["adam_lr"], hp["adam_beta1"], hp["adam_beta2"],
+                       hp["adam_eps"], hp["adam_weight_decay"])
+            done += k
+        adam_secs = time.perf_counter() - t
+        parts.append(f"AdamW on all {adam} elements ({adam_secs:.1f} s, timed in full)")
+    secs = total + adam_secs
+    return {"value": step_flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "plain C++ fp64 reference; one unit per shape bucket, scaled to m <= 1024 at the "
+                      "same aspect ratio and extrapolated by nominal NS FLOPs and unit count: "
+                      + "; ".join(parts),
+            "ms_per_step": 1e3 * secs, "extrapolated": True}
 
-    # plain C++ reference
-    t = time.perf_counter()
-    for (r, c), G in zip(shapes, grads):
-        _, U = cref.momentum(np.zeros((r, c)), G, hp["momentum"], hp["nesterov"])
-        O = cref.orthogonalize(U, hp["ns_steps"])
-        cref.weight_update(np.zeros((r, c)), O, hp["lr"], hp["weight_decay"], cref.muon_scale(r, c))
-    secs = time.perf_counter() - t
-    rate = flops / secs / 1e12
 
-    # numpy reference
-    ohp = oracle.OracleHparams(**{k: v for k, v in hp.items() if k in oracle.OracleHparams.__annotations__})
-    t = time.perf_counter()
-    for (r, c), G in zip(shapes, grads):
-        oracle.muon_step([(0, 1, r, c, 0, 0)], [np.zeros((r, c))], [G], [np.zeros((r, c))], [None], [None], ohp)
-    nsecs = time.perf_counter() - t
-    try:
-        from threadpoolctl import threadpool_info
-        ncores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:
-        ncores = os.cpu_count() or 1
-    label = ",".join(f"{r}x{c}" for r, c in shapes)
-    return {"value": rate, "unit": "TFLOP/s", "cores": cref.threads(), "kind": "oracle",
-            "sample": f"plain C++ fp64 reference, one Muon unit update (momentum, Newton-Schulz, "
-                      f"scaled update) per unit shape {label} of the workload "
-                      f"({flops / 1e12:.3f} TFLOP nominal, {secs:.1f} s)",
-            "extrapolated_ms_per_step": 1e3 * step_flops / (rate * 1e12),
-            "numpy_oracle": {"value": flops / nsecs / 1e12, "unit": "TFLOP/s", "cores": ncores,
-                             "seconds": nsecs}}
+def _cref_hparams(hp):
+    import oracle
+    return oracle.OracleHparams(**{k: v for k, v in hp.items() if k in oracle.OracleHparams.__annotations__})
 
 
 if __name__ == "__main__":

@@ -222,17 +222,17 @@ void ref_weight_update(double* W, const double* O, int64_t count, double lr, dou
   for (int64_t i = 0; i < count; ++i) W[i] = W[i] * (1.0 - lr * wd) - (lr * scale) * O[i];
 }
 
-// The AdamW backup of the [Moonlight] code, step t >= 1:
-// m <- m + (1 - b1)(g - m); v <- v + (1 - b2)(g^2 - v); u = m / (eps + sqrt(v));
-// W <- W (1 - lr wd) - lr sqrt(1 - b2^t) / (1 - b1^t) u  (eps outside the
-// bias correction, as printed).
+// The AdamW fallback for the parameters Muon does not take ([Moonlight]
+// "代码": the optimizer's AdamW backup), step t >= 1:
+//   m_t = b1 m + (1 - b1) g,  v_t = b2 v + (1 - b2) g^2,
+//   W_t = W (1 - lr wd) - lr sqrt(1 - b2^t) / (1 - b1^t) * m_t / (eps + sqrt(v_t))
+// (the bias corrections scale the step, so eps meets the uncorrected sqrt(v_t)).
 void ref_adamw(double* W, const double* g, double* m, double* v, int64_t count, int64_t t, double lr,
                double b1, double b2, double eps, double wd) {
-  const double bc1 = 1.0 - std::pow(b1, (double)t), bc2 = 1.0 - std::pow(b2, (double)t);
-  const double step = lr / (bc1 / std::sqrt(bc2));
+  const double step = lr * std::sqrt(1.0 - std::pow(b2, (double)t)) / (1.0 - std::pow(b1, (double)t));
   for (int64_t i = 0; i < count; ++i) {
-    m[i] = m[i] + (1.0 - b1) * (g[i] - m[i]);
-    v[i] = v[i] + (1.0 - b2) * (g[i] * g[i] - v[i]);
+    m[i] = b1 * m[i] + (1.0 - b1) * g[i];
+    v[i] = b2 * v[i] + (1.0 - b2) * g[i] * g[i];
     W[i] = W[i] * (1.0 - lr * wd) - step * (m[i] / (eps + std::sqrt(v[i])));
   }
 }

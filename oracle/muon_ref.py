@@ -75,8 +75,10 @@ def coeff_schedule(steps: int, coeffs: Optional[Sequence] = None) -> List[Tuple[
 def momentum_update(M: np.ndarray, G: np.ndarray, mu: float, nesterov: bool):
     """M_t = mu*M_{t-1} + G_t; the matrix to orthogonalize is G_t + mu*M_t
     with Nesterov ([Blog] "Variation of Muon Optimizer": msign(beta*M_t + G_t);
-    [Moonlight] code: ``buf.mul_(momentum).add_(g)`` then ``g.add(buf,
-    alpha=momentum)``), else M_t itself.  Returns (M_t, U)."""
+    the [Moonlight] "代码" section's step does the same: the buffer is
+    scaled by the momentum and the gradient added, then the gradient plus
+    the momentum times the buffer is orthogonalized), else M_t itself.
+    Returns (M_t, U)."""
     M = np.asarray(M, dtype=np.float64)
     G = np.asarray(G, dtype=np.float64)
     M_new = mu * M + G
@@ -201,31 +203,30 @@ def muon_scale(rows: int, cols: int, scale_dim: int = 0, rms_scale: float = RMS_
 
 def weight_update(W: np.ndarray, O: np.ndarray, lr: float, wd: float, scale: float) -> np.ndarray:
     """W_t = W_{t-1} - lr * (scale * O_t + wd * W_{t-1}) ([Moonlight]
-    "参数更新尺度调整" update formula), as the code applies it:
-    ``p.mul_(1 - lr*wd)`` then ``p.add_(u, alpha=-lr*scale)``."""
+    "参数更新尺度调整" update formula; "权重衰减机制": decoupled weight
+    decay), i.e. W_{t-1} (1 - lr wd) - lr scale O_t."""
     W = np.asarray(W, dtype=np.float64)
     return W * (1.0 - lr * wd) - (lr * scale) * np.asarray(O, dtype=np.float64)
 
 
 def adamw_update(W, g, m, v, t: int, lr: float, beta1: float, beta2: float,
                  eps: float, wd: float):
-    """The AdamW fallback of the [Moonlight] code ("AdamW backup"), step t >= 1:
-    m <- lerp(m, g, 1-beta1); v <- lerp(v, g^2, 1-beta2);
-    u = m / (eps + sqrt(v)); scale = (1-beta1^t) / sqrt(1-beta2^t);
-    W <- W (1 - lr wd) - (lr / scale) u.  eps sits outside the bias
-    correction exactly as printed.  Returns (W, m, v)."""
+    """The AdamW fallback for the parameters Muon does not take ([Moonlight]
+    "代码": the optimizer's AdamW backup), at step t >= 1, as mathematics:
+        m_t = beta1 m_{t-1} + (1 - beta1) g
+        v_t = beta2 v_{t-1} + (1 - beta2) g^2
+        W_t = W_{t-1} (1 - lr wd)
+              - lr sqrt(1 - beta2^t) / (1 - beta1^t) * m_t / (eps + sqrt(v_t))
+    The bias corrections multiply the step, so eps is added to the
+    uncorrected sqrt(v_t) (the page's placement; it differs from textbook
+    AdamW by eps sqrt(1 - beta2^t)).  Returns (W_t, m_t, v_t)."""
     W = np.asarray(W, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
-    m = np.asarray(m, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    m = m + (1.0 - beta1) * (g - m)
-    v = v + (1.0 - beta2) * (g * g - v)
-    u = m / (eps + np.sqrt(v))
-    bc1 = 1.0 - beta1 ** t
-    bc2 = 1.0 - beta2 ** t
-    scale = bc1 / math.sqrt(bc2)
-    W = W * (1.0 - lr * wd) - (lr / scale) * u
-    return W, m, v
+    m_t = beta1 * np.asarray(m, dtype=np.float64) + (1.0 - beta1) * g
+    v_t = beta2 * np.asarray(v, dtype=np.float64) + (1.0 - beta2) * g * g
+    step = lr * math.sqrt(1.0 - beta2 ** t) / (1.0 - beta1 ** t)
+    W_t = W * (1.0 - lr * wd) - step * (m_t / (eps + np.sqrt(v_t)))
+    return W_t, m_t, v_t
 
 
 # --------------------------------------------------------------------------

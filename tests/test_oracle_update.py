@@ -80,7 +80,7 @@ def test_adamw_step2_hand(impl):
     assert W2[0, 0] == pytest.approx(-1.0)
 
 
-def test_full_step_hand_2x3(golden_dir):
+def test_full_step_hand_2x3(golden_dir, impl):
     with open(os.path.join(golden_dir, "ns_diag_2x3.json")) as f:
         gold = json.load(f)
     G = np.array(gold["G"])
@@ -88,8 +88,8 @@ def test_full_step_hand_2x3(golden_dir):
     W = np.array([[0.1, -0.2, 0.3], [0.0, 0.5, -0.4]])
     hp = oracle.OracleHparams(lr=0.02, momentum=0.95, weight_decay=0.1, nesterov=True)
     table = [(0, 1, 2, 3, 0, 0)]
-    out = oracle.muon_step(table, [W], [G], [np.zeros((2, 3))], [None], [None], hp,
-                           want_updates=True)
+    out = impl.muon_step(table, [W], [G], [np.zeros((2, 3))], [None], [None], hp,
+                         want_updates=True)
     # M1 = G, U = 1.95 G, NS is scale invariant -> O; scale 0.2 sqrt(3)
     assert np.array_equal(out["M"][0], G)
     assert np.allclose(out["O"][0], O, atol=1e-14)
@@ -97,44 +97,87 @@ def test_full_step_hand_2x3(golden_dir):
     assert np.allclose(out["W"][0], exp, atol=1e-15)
 
 
-def test_split_units_are_independent():
+def test_split_units_are_independent(impl):
     r = np.random.default_rng(8)
     G = r.standard_normal((6, 4))
     W = r.standard_normal((6, 4))
     hp = oracle.OracleHparams()
     table = [(0, 1, 6, 4, 2, 0)]
-    out = oracle.muon_step(table, [W], [G], [np.zeros((6, 4))], [None], [None], hp,
-                           want_updates=True)
+    out = impl.muon_step(table, [W], [G], [np.zeros((6, 4))], [None], [None], hp,
+                         want_updates=True)
     for b in range(3):
-        Ob = oracle.orthogonalize((1 + hp.momentum) * G[2 * b:2 * b + 2])
+        Ob = impl.orthogonalize((1 + hp.momentum) * G[2 * b:2 * b + 2])
         assert np.allclose(out["O"][b], Ob, atol=1e-14)
-        sc = oracle.muon_scale(2, 4)
+        sc = impl.muon_scale(2, 4)
         exp = W[2 * b:2 * b + 2] * (1 - hp.lr * hp.weight_decay) - hp.lr * sc * Ob
         assert np.allclose(out["W"][0][2 * b:2 * b + 2], exp, atol=1e-14)
 
 
-def _bucket_summary(table, method=0):
-    units, keys, members = oracle.plan_buckets(table, method)
-    return [(k, len(mem)) for k, mem in zip(keys, members)], units, members
+def test_step_of_both_references_agrees():
+    """The whole step over a mixed table (split blocks, a tall unit with a
+    scale override, an AdamW vector), numpy reference against C++ one."""
+    r = np.random.default_rng(9)
+    table = [(0, 0, 12, 5, 4, 0), (0, 0, 9, 4, 0, 13), (1, 0, 1, 7, 0, 0)]
+    W = [r.standard_normal((t[2], t[3])) for t in table]
+    G = [r.standard_normal((t[2], t[3])) for t in table]
+    M = [r.standard_normal((t[2], t[3])) if t[0] == 0 else None for t in table]
+    EA = [None, None, r.standard_normal((1, 7))]
+    ES = [None, None, r.random((1, 7))]
+    hp = oracle.OracleHparams(adam_step=3)
+    a = oracle.muon_step(table, W, G, M, EA, ES, hp, want_updates=True)
+    b = cref.muon_step(table, W, G, M, EA, ES, hp, want_updates=True)
+    for k in ("W", "M", "exp_avg", "exp_avg_sq"):
+        for x, y in zip(a[k], b[k]):
+            if x is not None:
+                assert np.allclose(x, y, rtol=1e-12, atol=1e-14), k
+    assert sorted(a["O"]) == sorted(b["O"]) == list(range(4))
+    for i in a["O"]:
+        assert np.allclose(a["O"][i], b["O"][i], atol=1e-13)
 
 
-def test_plan_gpt2():
-    summ, units, members = _bucket_summary(configs.gpt2_small().table)
+def _bucket_summary(table, method=0, impl=oracle):
+    """[(key, count)] per bucket, plus the units in table order (numpy) or
+    bucket order (C++), from either reference's planner."""
+    if impl is oracle:
+        units, keys, members = oracle.plan_buckets(table, method)
+        return [(k, len(mem)) for k, mem in zip(keys, members)], units, members
+    units, buckets = cref.plan(table, method)
+    return [(tuple(b[:6]), b[7]) for b in buckets], units, None
+
+
+def test_plan_gpt2(impl):
+    summ, units, members = _bucket_summary(configs.gpt2_small().table, impl=impl)
     assert len(units) == 12 * 6
     assert summ == [((768, 768, 0, 1, 1, 0), 48), ((768, 3072, 1, 1, 1, 0), 12), ((768, 3072, 0, 1, 1, 0), 12)]
-    # units keep table order inside a bucket
-    for mem in members:
-        assert mem == sorted(mem)
-    assert [(u.param, u.row0) for u in units[:4]] == [(0, 0), (0, 768), (0, 1536), (1, 0)]
+    if members is not None:
+        # units keep table order inside a bucket
+        for mem in members:
+            assert mem == sorted(mem)
+        assert [(u.param, u.row0) for u in units[:4]] == [(0, 0), (0, 768), (0, 1536), (1, 0)]
+    else:
+        assert [tuple(u[:2]) for u in units[:4]] == [(0, 0), (0, 768), (0, 1536), (1, 0)]
 
 
-def test_plan_llama_and_moe():
-    summ, _, _ = _bucket_summary(configs.llama3_8b().table)
+def test_plan_llama_and_moe(impl):
+    summ, _, _ = _bucket_summary(configs.llama3_8b().table, impl=impl)
     assert summ == [((4096, 4096, 0, 1, 1, 0), 64), ((1024, 4096, 0, 1, 1, 0), 64),
                     ((4096, 14336, 1, 1, 1, 0), 64), ((4096, 14336, 0, 1, 1, 0), 32)]
-    summ, units, _ = _bucket_summary(configs.moe_grouped().table)
+    summ, units, _ = _bucket_summary(configs.moe_grouped().table, impl=impl)
     assert len(units) == 6656
     assert summ == [((128, 2048, 0, 1, 1, 0), 1664), ((1408, 2048, 0, 1, 1, 0), 3328),
                     ((1408, 2048, 1, 1, 1, 0), 1664)]
-    summ, _, _ = _bucket_summary(configs.wide_gram().table, 1)
+    summ, _, _ = _bucket_summary(configs.wide_gram().table, 1, impl=impl)
     assert summ == [((4096, 14336, 0, 1, 1, 1), 32), ((4096, 14336, 1, 1, 1, 1), 32)]
+
+
+def test_plan_gram_resolution_literal(impl):
+    """Method and compute dtype of Gram and auto requests, by hand: Gram's
+    fp16 chain only for m >= 512 and n >= 3m; outside, a bf16 request keeps
+    Gram in fp32 (dtype 0) and an fp32 request takes the standard method."""
+    table = [(0, 1, 512, 1536, 0, 0), (0, 1, 512, 1535, 0, 0), (0, 1, 511, 4096, 0, 0),
+             (0, 0, 300, 900, 0, 0), (0, 0, 1024, 4096, 0, 0)]
+    summ, _, _ = _bucket_summary(table, 1, impl=impl)
+    assert summ == [((512, 1536, 0, 1, 1, 1), 1), ((512, 1535, 0, 1, 0, 1), 1), ((511, 4096, 0, 1, 0, 1), 1),
+                    ((300, 900, 0, 0, 0, 0), 1), ((1024, 4096, 0, 0, 0, 1), 1)]
+    summ, _, _ = _bucket_summary(table, 2, impl=impl)
+    assert [k[4:] for k, _ in summ] == [(1, 1), (1, 0), (1, 0), (0, 0), (0, 1)]
