@@ -55,8 +55,10 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MomArgs a) {
   constexpr int CGS = KM_TC / 8;    // 8-column groups per tile row
   constexpr int RPP = 256 / CGS;    // rows per pass of the workgroup
   constexpr int NH = KM_TR / RPP;   // passes (rows per thread)
-  constexpr int NJ = KM_TC * (KM_TR / 8) / 256;  // transposed 8-element chunks per thread
-  static_assert(KM_TR == 64 && KM_TC % 64 == 0 && 256 % CGS == 0 && KM_TR % RPP == 0, "tile shape");
+  constexpr int CPT = KM_TR / 8;    // 8-element chunks per transposed row
+  constexpr int NJ = KM_TC * CPT / 256;  // transposed chunks per thread
+  static_assert(KM_TR % 64 == 0 && KM_TC % 64 == 0 && 256 % CGS == 0 && KM_TR % RPP == 0 &&
+                (KM_TC * CPT) % 256 == 0, "tile shape");
   __shared__ float tile[KM_TR][KM_TC + 1];
   __shared__ float red[4];
   const int unit = blockIdx.x / a.tilesPerUnit;
@@ -137,11 +139,12 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MomArgs a) {
     }
   }
   __syncthreads();
-  // transposed layout: row c0 + cc, columns r0 .. r0+64: KM_TC rows x 8 chunks of 8
+  // transposed layout: row c0 + cc, columns r0 .. r0 + KM_TR: KM_TC rows x CPT
+  // chunks of 8 (consecutive lanes write consecutive chunks of one row)
 #pragma unroll
   for (int j = 0; j < NJ && XT; ++j) {
     const int q = tid + 256 * j;
-    const int cc = q >> 3, rq = q & 7;
+    const int cc = q / CPT, rq = q % CPT;
     const int gc = c0 + cc, gr = r0 + rq * 8;
     if (gc < a.cols && gr < a.rows) {
       float u[8];
