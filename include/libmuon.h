@@ -260,6 +260,24 @@ muon_status ns_orthogonalize(void* X, int64_t rows, int64_t cols, int64_t ld, in
 muon_status ns_orthogonalize_workspace_bytes(int64_t rows, int64_t cols, int32_t dtype,
                                              int32_t method, size_t* bytes);
 
+/* ns_orthogonalize without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The arguments of ns_orthogonalize less
+ * the workspace; the same result and errors as
+ * ns_orthogonalize, with the same kernels; the scratch memory is a device
+ * array of MUON_NOALLOC_SCRATCH_BYTES inside the library, one per GPU the
+ * library is loaded on, held until the process ends.  The call allocates
+ * nothing: no hipMalloc / hipFree, no host staging.  Matrices whose
+ * ns_orthogonalize_workspace_bytes exceed MUON_NOALLOC_SCRATCH_BYTES (e.g. a
+ * bf16 2048 x 4096 fits, a 4096 x 4096 does not) return MUON_E_WORKSPACE
+ * before any launch.  Every call on one GPU uses that GPU's one array: calls
+ * that overlap in time on the same GPU (two streams, two threads) race and
+ * must be serialized by the caller.  The array's contents after a call are
+ * unspecified; nothing needs to be zero before one.  MUON_E_HIP if the
+ * array's device address cannot be obtained. */
+#define MUON_NOALLOC_SCRATCH_BYTES (64u << 20)
+muon_status ns_orthogonalize_noalloc(void* X, int64_t rows, int64_t cols, int64_t ld, int32_t dtype,
+                                     int32_t steps, const float* coeffs, int32_t method, void* stream);
 
 /* Optional per-kernel timing, for benchmarks.  While enabled (process-wide),
  * every kernel launch of the library is bracketed by two HIP events recorded

@@ -7,4 +7,5 @@ from ._lib import (EXPORTED, MUON_BF16, MUON_COEFF_HYBRID, MUON_COEFF_QUINTIC,  
                    lib, make_hparams, muon_ns_coefficients, muon_probe_copy, muon_probe_mfma,
                    muon_plan_buckets, muon_plan_create, muon_plan_units, muon_plan_workspace_bytes,
                    muon_status_string, muon_step, muon_timing_collect, muon_timing_enable,
-                   muon_version, ns_orthogonalize, ns_orthogonalize_workspace_bytes)
+                   muon_version, ns_orthogonalize, ns_orthogonalize_noalloc,
+                   ns_orthogonalize_workspace_bytes)

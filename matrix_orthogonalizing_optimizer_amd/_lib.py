@@ -28,7 +28,8 @@ EXPORTED = ["muon_plan_create", "muon_plan_destroy", "muon_plan_workspace_bytes"
             "muon_plan_buckets", "muon_plan_units", "muon_step", "ns_orthogonalize",
             "ns_orthogonalize_workspace_bytes", "muon_timing_enable", "muon_timing_collect",
             "muon_ns_coefficients", "muon_status_string", "muon_version", "muon_probe_mfma",
-            "muon_probe_copy"]
+            "muon_probe_copy", "ns_orthogonalize_noalloc"]
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MuonError(RuntimeError):
@@ -97,6 +98,9 @@ def lib():
     L.ns_orthogonalize.argtypes = [vp, i64, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float), i32, vp,
                                    sz, vp]
     L.ns_orthogonalize.restype = i32
+    L.ns_orthogonalize_noalloc.argtypes = [vp, i64, i64, i64, i32, i32, ctypes.POINTER(ctypes.c_float), i32,
+                                           vp]
+    L.ns_orthogonalize_noalloc.restype = i32
     L.ns_orthogonalize_workspace_bytes.argtypes = [i64, i64, i32, i32, ctypes.POINTER(sz)]
     L.ns_orthogonalize_workspace_bytes.restype = i32
     L.muon_timing_enable.argtypes = [i32]
@@ -342,6 +346,27 @@ def ns_orthogonalize(X, steps: int = 5, coeffs=None, method: int = MUON_NS_STAND
     _check("ns_orthogonalize",
            lib().ns_orthogonalize(_ptr(X), rows, cols, ld, dtype, steps,
                                   ca, method, _ptr(workspace), wsz, _stream(stream)))
+
+
+def ns_orthogonalize_noalloc(X, steps: int = 5, coeffs=None, method: int = MUON_NS_STANDARD,
+                             stream=None) -> None:
+    """ns_orthogonalize with the library's own device scratch array (no
+    workspace; nothing is allocated).  X: a 2-D fp32 or bf16 device tensor
+    with unit column stride."""
+    import torch
+    ca = _coeff_array(coeffs, steps)
+    di = _device_index(stream) if X.is_cuda else None
+    _check_device("X", X, di)
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be 2-D with unit column stride")
+    if X.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("X must be float32 or bfloat16")
+    rows, cols = X.shape
+    ld = X.stride(0) if rows > 1 else cols
+    dtype = MUON_F32 if X.dtype == torch.float32 else MUON_BF16
+    _check("ns_orthogonalize_noalloc",
+           lib().ns_orthogonalize_noalloc(_ptr(X), rows, cols, ld, dtype, steps, ca, method,
+                                          _stream(stream)))
 
 
 def muon_timing_enable(enable: bool = True) -> None:

@@ -15,7 +15,7 @@ BUILD = os.path.join(ROOT, "_build", "libmuon")
 LIB = os.path.join(PKG, "libmuon.so")
 
 HIP_SOURCES = ["api.cpp", "timing.cpp", "kernels_elem.hip", "gemm_bf16.hip", "gemm_f16.hip",
-               "gemm_f32.hip", "probes.hip"]
+               "gemm_f32.hip", "probes.hip", "noalloc.hip"]
 HOST_SOURCES = ["plan.cpp"]
 ARCH = "gfx950"
 
