@@ -42,8 +42,9 @@ def parse():
     p.add_argument("--no-probes", action="store_true",
                    help="skip the measured MFMA and copy ceilings")
     p.add_argument("--copy-calibration", action="store_true",
-                   help="only run the library's streaming copy of 1 GiB three times and exit: the "
-                        "reference dispatch that scales the FETCH_SIZE / WRITE_SIZE counters")
+                   help="only run the library's two streaming copies of 1 GiB (non-temporal, and through the "
+                        "GEMMs' global -> LDS loads) three times each and exit: the reference dispatches "
+                        "that scale the FETCH_SIZE / WRITE_SIZE counters")
     return p.parse_args()
 
 
@@ -66,9 +67,11 @@ def main():
         dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         for _ in range(3):
             mo.muon_probe_copy(src, dst, nbytes)
+        for _ in range(3):
+            mo.muon_probe_copy_lds(src, dst, nbytes)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": {"bytes_per_dispatch": nbytes, "dispatches": 3,
-                                               "kernel": "probe_copy_kernel"}}))
+                                               "kernels": ["probe_copy_kernel", "probe_copy_lds_kernel"]}}))
         return
     wl = configs.ALL[args.workload]()
     if args.ns_method:

@@ -319,6 +319,12 @@ muon_status muon_timing_collect(muon_kernel_timing* out, int32_t cap, int32_t* n
  *   or not 16-byte aligned; MUON_E_HIP if the launch fails. */
 muon_status muon_probe_mfma(int32_t workgroups, int32_t iters, float* sink, double* flops, void* stream);
 muon_status muon_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+/* muon_probe_copy_lds: the same copy through the Newton-Schulz GEMMs' load
+ *   path (global -> LDS with buffer_load_dwordx4 ... lds at the default cache
+ *   policy, then LDS -> global with ordinary 16-byte stores), one 16 KiB
+ *   block per workgroup; calibrates memory counters for those loads.  Same
+ *   arguments and errors as muon_probe_copy. */
+muon_status muon_probe_copy_lds(const void* src, void* dst, size_t bytes, void* stream);
 
 /* Newton-Schulz coefficient schedules: writes steps x 3 floats (a_k, b_k,
  * c_k) to out (capacity cap floats) for muon_hparams.coeffs.

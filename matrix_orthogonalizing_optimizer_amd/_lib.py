@@ -28,7 +28,7 @@ EXPORTED = ["muon_plan_create", "muon_plan_destroy", "muon_plan_workspace_bytes"
             "muon_plan_buckets", "muon_plan_units", "muon_step", "ns_orthogonalize",
             "ns_orthogonalize_workspace_bytes", "muon_timing_enable", "muon_timing_collect",
             "muon_ns_coefficients", "muon_status_string", "muon_version", "muon_probe_mfma",
-            "muon_probe_copy", "ns_orthogonalize_noalloc"]
+            "muon_probe_copy", "ns_orthogonalize_noalloc", "muon_probe_copy_lds"]
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -111,6 +111,8 @@ def lib():
     L.muon_probe_mfma.restype = i32
     L.muon_probe_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
     L.muon_probe_copy.restype = i32
+    L.muon_probe_copy_lds.argtypes = [vp, vp, ctypes.c_size_t, vp]
+    L.muon_probe_copy_lds.restype = i32
     L.muon_ns_coefficients.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_float), sz]
     L.muon_ns_coefficients.restype = i32
     L.muon_status_string.argtypes = [i32]
@@ -401,6 +403,14 @@ def muon_probe_copy(src, dst, nbytes: int, stream=None) -> None:
         if hasattr(t, "numel") and t.numel() * t.element_size() < nbytes:
             raise ValueError("buffer smaller than nbytes")
     _check("muon_probe_copy", lib().muon_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+def muon_probe_copy_lds(src, dst, nbytes: int, stream=None) -> None:
+    """Enqueue the streaming copy through the GEMMs' global -> LDS load path."""
+    for t in (src, dst):
+        if hasattr(t, "numel") and t.numel() * t.element_size() < nbytes:
+            raise ValueError("buffer smaller than nbytes")
+    _check("muon_probe_copy_lds", lib().muon_probe_copy_lds(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
 
 
 def muon_status_string(status: int) -> str:

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
+#include "gemm.hpp"
 #include "libmuon.h"
 
 namespace muon {
@@ -62,6 +63,30 @@ __global__ __launch_bounds__(256) void probe_copy_kernel(const u32x4* __restrict
     if (base + u * 256 < n16) __builtin_nontemporal_store(v[u], dst + base + u * 256);
 }
 
+// The same streaming copy with the GEMMs' load path: global -> LDS with
+// buffer_load_dwordx4 ... lds at the default cache policy (each lane's 16
+// bytes land at the wave's LDS base + 16 * lane), then LDS -> global with
+// ordinary 16-byte stores.  Calibrates the memory counters for the loads the
+// Newton-Schulz GEMMs issue.
+__global__ __launch_bounds__(256) void probe_copy_lds_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                             int64_t n16) {
+  __shared__ u32x4 buf[256 * kUnroll];
+  const int64_t base = (int64_t)blockIdx.x * 256 * kUnroll;
+  const int64_t left = n16 - base;
+  const int64_t here = left < 256 * kUnroll ? left : 256 * kUnroll;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(src + base, (uint32_t)(here * 16));
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    copy16_to_lds(r, &buf[u * 256 + wave * 64], (uint32_t)((u * 256 + wave * 64 + lane) * 16));
+  wait_vmcnt<0>();
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u)
+    if (u * 256 + (int)threadIdx.x < here) dst[base + u * 256 + threadIdx.x] = buf[u * 256 + threadIdx.x];
+}
+
 }  // namespace
 }  // namespace muon
 
@@ -85,6 +110,19 @@ muon_status muon_probe_copy(const void* src, void* dst, size_t bytes, void* stre
   const unsigned grid = (unsigned)blocks;
   hipLaunchKernelGGL(muon::probe_copy_kernel, dim3(grid), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
                      reinterpret_cast<const muon::u32x4*>(src), reinterpret_cast<muon::u32x4*>(dst), n16);
+  return hipGetLastError() == hipSuccess ? MUON_OK : MUON_E_HIP;
+}
+
+muon_status muon_probe_copy_lds(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst || bytes == 0 || (bytes & 15) != 0 || ((uintptr_t)src & 15) != 0 ||
+      ((uintptr_t)dst & 15) != 0)
+    return MUON_E_ARG;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  const int64_t blocks = (n16 + 256 * muon::kUnroll - 1) / (256 * muon::kUnroll);
+  if (blocks > 0x7fffffff) return MUON_E_ARG;
+  hipLaunchKernelGGL(muon::probe_copy_lds_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const muon::u32x4*>(src),
+                     reinterpret_cast<muon::u32x4*>(dst), n16);
   return hipGetLastError() == hipSuccess ? MUON_OK : MUON_E_HIP;
 }
 
