@@ -287,3 +287,49 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError, match="device memory"):
         mo.muon_step(plan, [p], [p.clone()], [torch.zeros(4, 8)], [None], [None], hp,
                      torch.empty(mo.muon_plan_workspace_bytes(plan), dtype=torch.uint8))
+
+
+def _random_table(rng, n):
+    rows = []
+    for _ in range(n):
+        kind = int(rng.integers(0, 2))
+        dt = int(rng.integers(0, 2))
+        if kind == 1:
+            rows.append((1, dt, int(rng.choice([1, 3, 64])), int(rng.integers(0, 300)), 0, 0))
+            continue
+        shape = [int(rng.choice([0, 1, 7, 64, 128, 300, 512, 600, 1536, 1800, 2048])) for _ in range(2)]
+        split = 0
+        if shape[0] > 0 and rng.random() < 0.3:
+            divs = [h for h in (1, 2, 3, 4, 64, 128, 256) if shape[0] % h == 0]
+            split = int(rng.choice(divs))
+        sd = int(rng.choice([0, 0, 0, 11, 4096]))
+        rows.append((0, dt, shape[0], shape[1], split, sd))
+    return rows
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_plan_random_tables_match_both_references(seed):
+    """Random shape tables (empty, tiny, ragged, split, tall, wide, repeated
+    shapes; every method and compute-dtype option): the library's plan equals
+    both references' independent planners bit for bit."""
+    _lib_or_skip()
+    import numpy as np
+    rng = np.random.default_rng(1000 + seed)
+    table = _random_table(rng, int(rng.integers(1, 25)))
+    for method in (0, 1, 2):
+        for ns_dtype in (-1, 0, 1):
+            plan = mo.muon_plan_create(table, method, ns_dtype)
+            units, keys, members = oracle.plan_buckets(table, method, ns_dtype)
+            exp_b, first = [], 0
+            for k, mem in zip(keys, members):
+                exp_b.append(tuple(k) + (first, len(mem)))
+                first += len(mem)
+            exp_u = [(units[ui].param, units[ui].row0, units[ui].rows, units[ui].cols, int(units[ui].tall),
+                      units[ui].scale_dim if units[ui].scale_dim > 0 else max(units[ui].rows, units[ui].cols))
+                     for mem in members for ui in mem]
+            assert mo.muon_plan_buckets(plan) == exp_b, (seed, method, ns_dtype)
+            assert mo.muon_plan_units(plan) == exp_u, (seed, method, ns_dtype)
+            c_units, c_buckets = cref.plan(table, method, ns_dtype)
+            assert c_buckets == exp_b and c_units == exp_u, (seed, method, ns_dtype)
+            has_work = bool(exp_u) or any(r[0] == 1 for r in table)
+            assert (mo.muon_plan_workspace_bytes(plan) > 0) == has_work
