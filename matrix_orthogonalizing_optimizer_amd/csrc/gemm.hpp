@@ -13,10 +13,13 @@
 // upper-triangle tiles are computed, then mirrored), and the update is
 // computed transposed, Y' = Y P^T (P is symmetric).
 //
-// Tiling (CDNA4, wave64): a 256-thread workgroup owns a BM x BN output tile
-// (256 x 256, or 128 x 128 for small m); 2 x 2 waves each own (BM/2) x (BN/2)
-// built from 32x32 MFMA tiles (v_mfma_f32_32x32x16_{bf16,f16}; fp32 issues
-// four v_mfma_f32_32x32x2_f32 per 16-byte fragment), accumulators in AGPRs.
+// Tiling (CDNA4, wave64): a workgroup of NW waves owns a BM x BN output tile
+// (256 x 256, or 128 x 128 for small m); 2 x (NW / 2) waves each own (BM/2) x
+// (2 BN / NW) built from 32x32 MFMA tiles (v_mfma_f32_32x32x16_{bf16,f16}; fp32
+// issues four v_mfma_f32_32x32x2_f32 per 16-byte fragment).  NW = 4: one wave
+// per SIMD, 128 x 128 accumulators in AGPRs; NW = 8: two waves per SIMD, 128 x
+// 64 each (the compiler keeps them in VGPRs), so one wave's MFMAs can issue
+// while the other waits on a memory instruction.
 //
 // Operand staging: K advances 128 bytes per row per stage (whole cache
 // lines: the vector L1 keeps a bounded number of line requests in flight, so
@@ -290,8 +293,8 @@ template <int B, int E, typename F> __device__ __forceinline__ void static_for(F
 // s_waitcnt lgkmcnt(0) alone.
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
-template <int BM, int BN, typename TI, typename TO, bool SYM, int EPI, bool TRANS = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int BM, int BN, typename TI, typename TO, bool SYM, int EPI, bool TRANS = false, int NW = 4>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void gemm_kernel(const GemmArgs a) {
   constexpr int ES = (int)sizeof(TI);
   constexpr int EPC = 16 / ES;            // elements per 16-byte chunk
@@ -299,26 +302,30 @@ void gemm_kernel(const GemmArgs a) {
   constexpr int BK = CPR * EPC;           // K elements per stage
   constexpr int NSTG = 2;                 // stages in the LDS ring
   constexpr int NSTEP = CPR / 2;          // MFMA k-steps per stage (one chunk per lane half)
-  constexpr int WTM = BM / 64;            // 32x32 tiles per wave along M
-  constexpr int WTN = BN / 64;            // ... along N
-  constexpr int WN = BN / 2;              // wave sub-tile width
+  // NW waves: 2 along M by NW / 2 along N; NW / 2 of them copy each operand
+  constexpr int WGN = NW / 2;             // waves along N
+  constexpr int WPO = NW / 2;             // waves copying one operand
+  constexpr int WTM = BM / 64;            // 32x32 tiles per wave along M (BM / 2 rows)
+  constexpr int WN = BN / WGN;            // wave sub-tile width
+  constexpr int WTN = WN / 32;            // 32x32 tiles per wave along N
   constexpr int STG = (BM + BN) * CPR;    // 16-byte slots per stage
-  constexpr int NQ = STG / 256;           // copy instructions per wave per stage (8 rows each)
+  constexpr int NQ = STG / (64 * NW);     // copy instructions per wave per stage (8 rows each)
   constexpr int NDR = WTM + WTN;          // fragment reads per k-step
   constexpr int NPAIR = WTM * WTN;        // fragment pairs per k-step
   constexpr int CPP = (NQ + NPAIR - 1) / NPAIR;  // copies issued per MFMA pair
   constexpr int SROW = WN + 8;            // epilogue strip row stride (floats)
   static_assert(BM == BN, "square tiles");
-  static_assert(NQ * 8 == BM / 2, "each wave copies half of one operand's rows");
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(NQ * 8 * WPO == BM, "each wave copies 1 / WPO of one operand's rows");
   static_assert(NDR <= NPAIR, "fragment reads fit between the MFMAs of one step");
-  static_assert(4 * 32 * SROW * 4 <= NSTG * STG * 16, "epilogue strips fit in the ring");
+  static_assert(NW * 32 * SROW * 4 <= NSTG * STG * 16, "epilogue strips fit in the ring");
 
   __shared__ u32x4 ring[NSTG][STG];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: operand choice and buffer resource stay scalar
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / WGN, wn = wid % WGN;
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -380,14 +387,15 @@ void gemm_kernel(const GemmArgs a) {
   // = 8 rows x 8 chunks; lane l lands in row 8q + l/8 (of the wave's half)
   // at physical chunk l % 8, which holds logical chunk (l % 8) ^ swz(row),
   // swz(row) = (row & 7) ^ ((row >> 3) & 1) = (l / 8) ^ (q & 1).
-  const bool copiesL = wid < 2;
+  const bool copiesL = wid < WPO;
   const TI* P = reinterpret_cast<const TI*>(copiesL ? a.L : a.R) +
                 (int64_t)unit * (copiesL ? a.sL : a.sR);
   const int64_t ld = copiesL ? a.ldl : a.ldr;
   const int prows = copiesL ? a.M : a.N;
-  const int slot_off = (copiesL ? 0 : BM * CPR) + (wid & 1) * (BM / 2) * CPR;
+  const int cw = wid % WPO;  // this wave's share of its operand's rows
+  const int slot_off = (copiesL ? 0 : BM * CPR) + cw * (BM / WPO) * CPR;
   // row-major operand (TRANS = false)
-  const int crow = (copiesL ? row0 : col0) + (wid & 1) * (BM / 2) + (lane >> 3);  // operand row of copy 0
+  const int crow = (copiesL ? row0 : col0) + cw * (BM / WPO) + (lane >> 3);  // operand row of copy 0
   const int ck0 = ((lane & 7) ^ (lane >> 3)) * EPC;        // k of this lane's chunk, even copies
   const int ck1 = ((lane & 7) ^ (lane >> 3) ^ 1) * EPC;    // odd copies
   const uint32_t cb0 = (uint32_t)(((int64_t)crow * ld + ck0) * ES);
@@ -414,7 +422,7 @@ void gemm_kernel(const GemmArgs a) {
   if constexpr (TRANS && ES == 2) {
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
-      const int krow = ((wid & 1) * NQ + par) * RPC + lane / CR;
+      const int krow = (cw * NQ + par) * RPC + lane / CR;
       const int col = c0op + ((lane % CR) ^ swz_t(krow)) * EPC;
       tb[par] = col < prows ? (uint32_t)(((int64_t)krow * ld + col) * ES) : 0x80000000u;
     }
@@ -426,7 +434,7 @@ void gemm_kernel(const GemmArgs a) {
     if constexpr (TRANS && ES == 2) {
       off = tb[q & 1] + (uint32_t)(((int64_t)((q & ~1) * RPC + k0) * ld) * ES);
     } else if constexpr (TRANS) {
-      const int slot = ((wid & 1) * NQ + q) * 64 + lane;
+      const int slot = (cw * NQ + q) * 64 + lane;
       const int krow = slot / CR;
       const int lc = (slot % CR) ^ swz_t(krow);
       const int col = c0op + lc * EPC;
@@ -625,8 +633,8 @@ void gemm_kernel(const GemmArgs a) {
   // bits of the direct pass, and reads 2 instructions instead of 8
   constexpr bool MIR16 = sizeof(TO) == 2;
   constexpr int RS16 = WN * 2 + 32;
-  static_assert(4 * 32 * SROW * 4 + 4 * 32 * RS16 <= NSTG * STG * 16, "16-bit strips fit in the ring");
-  char* strip16 = reinterpret_cast<char*>(&ring[0][0]) + 4 * 32 * SROW * 4 + wid * (32 * RS16);
+  static_assert(NW * 32 * SROW * 4 + NW * 32 * RS16 <= NSTG * STG * 16, "16-bit strips fit in the ring");
+  char* strip16 = reinterpret_cast<char*>(&ring[0][0]) + NW * 32 * SROW * 4 + wid * (32 * RS16);
   const int gc0 = col0 + wn * WN;  // global column of strip column 0
 
   // Each pass covers the 32 x WN strip of MFMA row-tile i in NT rounds of 64

@@ -5,9 +5,9 @@
 namespace muon {
 
 namespace {
-template <int T, typename TO, bool SYM, int EPI, bool TRANS = false>
+template <int T, typename TO, bool SYM, int EPI, bool TRANS = false, int NW = 4>
 hipError_t go(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<T, T, float, TO, SYM, EPI, TRANS>), dim3(a.totalTiles), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_kernel<T, T, float, TO, SYM, EPI, TRANS, NW>), dim3(a.totalTiles), dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
