@@ -56,8 +56,8 @@ typedef enum {
  * R scaled by a power of two only where that stays within the bf16
  * tolerance on the workload gradients, m >= 512 and n >= 3m.  An explicit
  * MUON_NS_GRAM outside that region is served in a precision that meets the
- * tolerance of the requested compute dtype: with bf16 the Gram chain runs
- * in fp32 (the bucket reports compute dtype MUON_F32); with fp32 the unit
+ * tolerance of the requested compute dtype: with bf16 the unit's Gram
+ * iteration runs in fp32 (the bucket reports compute dtype MUON_F32); with fp32 the unit
  * runs the standard iteration (the bucket reports MUON_NS_STANDARD), since
  * an fp32 Gram chain there exceeds the fp32 tolerance.  MUON_NS_AUTO picks
  * Gram exactly inside the region, where it also does less work (executed
