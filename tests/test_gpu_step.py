@@ -342,11 +342,13 @@ def test_ragged_unaligned_buffers(pdt):
     """Unaligned parameter, gradient, momentum and update_out buffers (storage
     offset of one element) with ragged shapes, a wide 300 x 701 and a tall
     701 x 300 unit, and an AdamW parameter of 1001 elements: the element-wise
-    load/store paths of the momentum, fused-update and AdamW kernels.  W, M,
-    O, m and v against the numpy reference."""
+    load/store paths of the momentum, fused-update and AdamW kernels; the
+    wide unit carries a scale_dim override.  W, M, O, m and v against the
+    numpy reference."""
     print(f"muon_step ragged unaligned pdt={pdt}", flush=True)
     d = dev()
-    table = [(0, pdt, 300, 701, 0, 0), (0, pdt, 701, 300, 0, 0), (1, pdt, 1, 1001, 0, 0)]
+    # the wide unit also overrides the scale dimension (scale 0.2 sqrt(1000))
+    table = [(0, pdt, 300, 701, 0, 1000), (0, pdt, 701, 300, 0, 0), (1, pdt, 1, 1001, 0, 0)]
     wl = configs.Workload("ragged", table, ["wide", "tall", "vec"], rank=8, hp=configs._hp())
     P0, M0, EA0, ES0 = gen.make_state(wl, "cpu")
     G0 = gen.make_grads(wl, 0, "cpu")
