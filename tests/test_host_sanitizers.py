@@ -1,0 +1,157 @@
+"""Host code under the compiler's sanitizers (CPU only, no GPU).
+
+The library's planner (csrc/plan.cpp, host-only C++) and the plain C++ fp64
+reference (oracle/muon_ref.cpp) are built with g++ into two separate
+executables under -fsanitize=address,undefined (and the reference also under
+-fsanitize=thread, running its threaded products with several workers):
+
+- every workload table, with each Newton-Schulz method and compute dtype, is
+  planned by both; the units and buckets they print must agree line for line,
+  and no sanitizer may report;
+- seeded random tables (ragged sizes, row splits, both dtypes, both kinds) the
+  same;
+- malformed tables are rejected by the planner with an error status and no
+  sanitizer report;
+- every reference routine runs on awkward shapes (1 x 1, 1 x n, empty,
+  ragged, tall and wide, zero input) without a report and with finite output.
+The two executables share no source file.
+"""
+import os
+import random
+import shutil
+import subprocess
+
+import pytest
+
+from workloads import configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "matrix_orthogonalizing_optimizer_amd", "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+CDIR = os.path.join(ROOT, "tests", "c")
+ORACLE_SRC = os.path.join(ROOT, "oracle", "muon_ref.cpp")
+
+ENV = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:halt_on_error=1",
+           UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1", TSAN_OPTIONS="halt_on_error=1")
+ENV.pop("LD_PRELOAD", None)
+SAN_MARKERS = ("Sanitizer", "runtime error:")
+
+
+def _build(out, sources, flags, includes=()):
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-pthread"] + flags
+    cmd += [f"-I{d}" for d in includes] + sources + ["-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    return out
+
+
+@pytest.fixture(scope="module")
+def exes(tmp_path_factory):
+    if shutil.which("g++") is None:
+        pytest.skip("g++ not available")
+    d = tmp_path_factory.mktemp("san")
+    probe_src = d / "probe.cpp"
+    probe_src.write_text("int main() { return 0; }\n")
+    asan = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+    try:
+        probe = _build(str(d / "probe"), [str(probe_src)], asan)
+        if subprocess.run([probe], env=ENV, capture_output=True).returncode != 0:
+            raise AssertionError("probe did not run")
+    except AssertionError as e:
+        pytest.skip(f"address sanitizer unusable here: {e}")
+    return {
+        "plan": _build(str(d / "plan_asan"), [os.path.join(CDIR, "plan_host_check.cpp"),
+                                                os.path.join(CSRC, "plan.cpp")], asan, [INCLUDE, CSRC]),
+        "oracle": _build(str(d / "oracle_asan"), [os.path.join(CDIR, "oracle_host_check.cpp"), ORACLE_SRC], asan),
+        "oracle_tsan": _build(str(d / "oracle_tsan"), [os.path.join(CDIR, "oracle_host_check.cpp"), ORACLE_SRC],
+                              ["-fsanitize=thread"]),
+    }
+
+
+def _run(cmd, stdin=""):
+    r = subprocess.run(cmd, input=stdin, env=ENV, capture_output=True, text=True, timeout=600)
+    assert not any(m in r.stderr for m in SAN_MARKERS), r.stderr[-4000:]
+    assert r.returncode == 0, (r.returncode, r.stderr[-2000:])
+    return r.stdout
+
+
+def _tables_text(cases):
+    lines = []
+    for table, method, nsd in cases:
+        lines.append(f"{len(table)} {method} {nsd}")
+        lines += [" ".join(str(int(x)) for x in row) for row in table]
+    return "\n".join(lines) + "\n"
+
+
+def _plans(stdout, keep=("status", "unit", "bucket", "end")):
+    plans, cur = [], []
+    for line in stdout.splitlines():
+        if line.split(" ", 1)[0] in keep:
+            cur.append(line)
+        if line == "end":
+            plans.append(cur)
+            cur = []
+    return plans
+
+
+def _compare(exes, cases):
+    text = _tables_text(cases)
+    lib = _plans(_run([exes["plan"]], text))
+    ref = _plans(_run([exes["oracle"], "plan"], text))
+    assert len(lib) == len(ref) == len(cases)
+    for (table, method, nsd), a, b in zip(cases, lib, ref):
+        assert a[0] == "status 0", (method, nsd, a[0])
+        assert a == b, (method, nsd, len(table))
+
+
+@pytest.mark.parametrize("name", sorted(configs.ALL))
+def test_workload_plans_agree_under_sanitizers(exes, name):
+    table = configs.ALL[name]().table
+    _compare(exes, [(table, method, nsd) for method in (0, 1, 2) for nsd in (-1, 0, 1)])
+
+
+def test_random_tables_agree_under_sanitizers(exes):
+    rng = random.Random(20261203)
+    cases = []
+    for _ in range(60):
+        table = []
+        for _ in range(rng.randint(0, 12)):
+            kind, dt = rng.randint(0, 1), rng.randint(0, 1)
+            rows = rng.choice([0, 1, 2, 7, 64, 127, 128, 300, 512, 768, 1100, 2048, 3072])
+            cols = rng.choice([0, 1, 3, 64, 129, 256, 700, 1536, 3000, 4096])
+            split = 0
+            if kind == 0 and rows > 1 and rng.random() < 0.3:
+                split = rng.choice([h for h in (1, 2, 4, 8, 16, 64, 128) if rows % h == 0] or [0])
+            sd = rng.choice([0, 0, 0, 5, 4096])
+            table.append((kind, dt, rows, cols, split, sd))
+        cases.append((table, rng.randint(0, 2), rng.choice([-1, 0, 1])))
+    _compare(exes, cases)
+
+
+def test_malformed_tables_rejected_under_sanitizers(exes):
+    bad = [
+        ([(0, 1, -1, 4, 0, 0)], 0, -1),          # negative rows
+        ([(0, 1, 4, 4, 0, -3)], 0, -1),          # negative scale_dim
+        ([(0, 1, 6, 4, 4, 0)], 0, -1),           # split does not divide rows
+        ([(1, 1, 8, 4, 4, 0)], 0, -1),           # AdamW parameter with a split
+        ([(2, 1, 8, 4, 0, 0)], 0, -1),           # unknown kind
+        ([(0, 3, 8, 4, 0, 0)], 0, -1),           # unknown dtype
+        ([(0, 1, (1 << 30) + 1, 8, 0, 0)], 0, -1),  # past the dimension limit
+        ([(0, 1, 8, 4, 0, 0)], 5, -1),           # unknown method
+        ([(0, 1, 8, 4, 0, 0)], 0, 4),            # unknown compute dtype
+        ([(0, 1, 100000, 100000, 0, 0)], 0, -1),  # one operand past 2^31 bytes
+    ]
+    out = _plans(_run([exes["plan"]], _tables_text(bad)))
+    assert len(out) == len(bad)
+    for case, lines in zip(bad, out):
+        assert lines[0] != "status 0" and lines[1:] == ["end"], (case, lines)
+
+
+def test_reference_routines_under_address_sanitizer(exes):
+    out = _run([exes["oracle"], "math", "4"])
+    assert out.splitlines()[-1] == "math ok"
+
+
+def test_reference_threads_under_thread_sanitizer(exes):
+    out = _run([exes["oracle_tsan"], "math", "4"])
+    assert out.splitlines()[-1] == "math ok"
