@@ -188,6 +188,13 @@ def _check_device(name, t, device_index):
         raise ValueError(f"{name}: on {t.device}, the kernels run on cuda:{device_index}")
 
 
+def _check_call_device(name, t, stream):
+    """_check_device against the call's GPU, looked up only for device tensors."""
+    if t is None or isinstance(t, int) or not hasattr(t, "data_ptr"):
+        return
+    _check_device(name, t, _device_index(stream) if t.is_cuda else None)
+
+
 class Plan:
     """Owns a muon_plan handle (released on close / garbage collection)."""
 
@@ -342,7 +349,7 @@ def ns_orthogonalize(X, steps: int = 5, coeffs=None, method: int = MUON_NS_STAND
         if workspace is None:
             nb = ns_orthogonalize_workspace_bytes(rows, cols, dtype, method)
             workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=X.device)
-    wsz = workspace.numel() if hasattr(workspace, "numel") else 0
+    wsz = workspace.numel() * workspace.element_size() if hasattr(workspace, "numel") else 0
     if isinstance(workspace, tuple):
         workspace, wsz = workspace
     _check("ns_orthogonalize",
@@ -389,7 +396,8 @@ def muon_timing_collect() -> dict:
 def muon_probe_mfma(workgroups: int, iters: int, sink, stream=None) -> float:
     """Enqueue the register-only bf16 MFMA loop; returns its FLOPs.  sink:
     device tensor of at least `workgroups` float32."""
-    if hasattr(sink, "numel") and sink.numel() < workgroups:
+    _check_call_device("sink", sink, stream)
+    if hasattr(sink, "numel") and sink.numel() * sink.element_size() < 4 * workgroups:
         raise ValueError("sink holds fewer than `workgroups` floats")
     flops = ctypes.c_double()
     _check("muon_probe_mfma", lib().muon_probe_mfma(workgroups, iters, _ptr(sink), ctypes.byref(flops),
@@ -397,19 +405,22 @@ def muon_probe_mfma(workgroups: int, iters: int, sink, stream=None) -> float:
     return flops.value
 
 
-def muon_probe_copy(src, dst, nbytes: int, stream=None) -> None:
-    """Enqueue the streaming copy of nbytes from src to dst (device tensors)."""
-    for t in (src, dst):
+def _check_copy_buffers(src, dst, nbytes, stream):
+    for name, t in (("src", src), ("dst", dst)):
+        _check_call_device(name, t, stream)
         if hasattr(t, "numel") and t.numel() * t.element_size() < nbytes:
             raise ValueError("buffer smaller than nbytes")
+
+
+def muon_probe_copy(src, dst, nbytes: int, stream=None) -> None:
+    """Enqueue the streaming copy of nbytes from src to dst (device tensors)."""
+    _check_copy_buffers(src, dst, nbytes, stream)
     _check("muon_probe_copy", lib().muon_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
 
 
 def muon_probe_copy_lds(src, dst, nbytes: int, stream=None) -> None:
     """Enqueue the streaming copy through the GEMMs' global -> LDS load path."""
-    for t in (src, dst):
-        if hasattr(t, "numel") and t.numel() * t.element_size() < nbytes:
-            raise ValueError("buffer smaller than nbytes")
+    _check_copy_buffers(src, dst, nbytes, stream)
     _check("muon_probe_copy_lds", lib().muon_probe_copy_lds(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
 
 

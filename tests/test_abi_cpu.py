@@ -287,6 +287,13 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError, match="device memory"):
         mo.muon_step(plan, [p], [p.clone()], [torch.zeros(4, 8)], [None], [None], hp,
                      torch.empty(mo.muon_plan_workspace_bytes(plan), dtype=torch.uint8))
+    host = torch.zeros(1 << 12, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="device memory"):
+        mo.muon_probe_copy(host, host.clone(), 1 << 12)
+    with pytest.raises(ValueError, match="device memory"):
+        mo.muon_probe_copy_lds(host, host.clone(), 1 << 12)
+    with pytest.raises(ValueError, match="device memory"):
+        mo.muon_probe_mfma(4, 8, torch.zeros(4))
 
 
 def _random_table(rng, n):
