@@ -512,6 +512,12 @@ void gemm_kernel(const GemmArgs a) {
     if (r < WTM) fa[slot][r] = v;
     else fb[slot][r - WTM] = v;
   };
+  // p-th fragment read of a k-step (row-major operands): the fragment the
+  // MFMA sequence (j fastest) needs p-th for the first time, A0, B0 ..
+  // B(WTN-1), A1 .. A(WTM-1), so the next step's first MFMA waits for two
+  // reads rather than for all of them (update and fused update 0.3-0.5%
+  // faster).  K-major reads are all waited for at once and keep their order.
+  auto ro = [](int p) { return TRANS ? p : (p == 0 ? 0 : (p <= WTN ? WTM + p - 1 : p - WTN)); };
   auto mfma_pair = [&](int p, int slot) {
     const int i = p / WTN, j = p % WTN;
     Mfma<TI>::run(acc[i][j], fa[slot][i], fb[slot][j]);
@@ -540,7 +546,7 @@ void gemm_kernel(const GemmArgs a) {
   wait_vmcnt<NQ3>();
   __syncthreads();
 #pragma unroll
-  for (int r = 0; r < NDR; ++r) read_one(r, 0, 0, 0);
+  for (int r = 0; r < NDR; ++r) read_one(ro(r), 0, 0, 0);
 
   // transposed 16-bit reads are not tracked by the compiler: wait for them
   // explicitly before the MFMAs of the step they feed
@@ -555,7 +561,7 @@ void gemm_kernel(const GemmArgs a) {
 #pragma unroll
       for (int p = 0; p < NPAIR; ++p) {
         mfma_pair(p, s & 1);
-        if (p < NDR) read_one(p, kt, s + 1, (s + 1) & 1);
+        if (p < NDR) read_one(ro(p), kt, s + 1, (s + 1) & 1);
         if constexpr (SPLIT) {
           const int qq = s * (NPAIR - NDR) + (p - NDR);
           if (p >= NDR && qq < NQR) copy_one(NQ3 + qq, kt + 1);
@@ -581,7 +587,7 @@ void gemm_kernel(const GemmArgs a) {
         for (int c = 0; c < CPP; ++c)
           if (p * CPP + c < NQ) copy_one(p * CPP + c, kt + 2);
       }
-      if (p < NDR) read_one(p, kt + 1, 0, 0);
+      if (p < NDR) read_one(ro(p), kt + 1, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }

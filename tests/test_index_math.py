@@ -132,3 +132,22 @@ def test_lds_plan_in_bounds(BM, NW, ES, TRANS):
             L = lane & 15
             off = (c8 + (L >> 2)) * RS16 + (jj - L + 4 * (L & 3)) * 2
             assert 0 <= off and off + 4 * RS16 + 8 <= 32 * RS16
+
+
+@pytest.mark.parametrize("WTM,WTN", [(4, 4), (4, 2), (2, 2)])
+def test_fragment_read_order(WTM, WTN):
+    """The row-major read order is a permutation of the fragments, and each
+    MFMA of the sequence (j fastest) finds both its fragments among the reads
+    issued before the first MFMA that needs a later one."""
+    ro = [0 if p == 0 else (WTM + p - 1 if p <= WTN else p - WTN) for p in range(WTM + WTN)]
+    assert sorted(ro) == list(range(WTM + WTN))
+    pos = {r: k for k, r in enumerate(ro)}
+    need = 0
+    for q in range(WTM * WTN):
+        i, j = q // WTN, q % WTN
+        need = max(need, pos[i], pos[WTM + j])
+        # reads needed by the first q + 1 MFMAs are a prefix no longer than
+        # the fragments those MFMAs touch
+        touched = {i2 for i2 in range(q // WTN + 1)} | {WTM + j2 for j2 in range(min(q + 1, WTN))}
+        assert need + 1 == len(touched)
+
