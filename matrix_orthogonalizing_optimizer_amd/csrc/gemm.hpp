@@ -662,17 +662,26 @@ void gemm_kernel(const GemmArgs a) {
   // Each pass covers the 32 x WN strip of MFMA row-tile i in NT rounds of 64
   // lanes x 8 elements.  Direct pass: with CW = WN / 8 chunks per strip row,
   // lane l covers rows l / CW + (64 / CW) t at columns 8 (l % CW) .. +7.
-  // Mirror pass: strip column jj = (64 t + l) % WN, rows c8 .. c8 + 7 with
-  // c8 = 8 ((64 t + l) / WN).
+  // Mirror pass: strip column jj, rows c8 .. c8 + 7.  16-bit: jj = 16 t +
+  // l % 16, c8 = 8 (l / 16), so that the four 16-lane groups of a store (a
+  // transposed read serves 16 columns at one c8) write the same 16 output
+  // rows, 64 contiguous bytes each, instead of 64 rows of 16 bytes (the
+  // polynomial and the Gram chain's products 2-3% faster).  fp32: jj =
+  // (64 t + l) % WN, c8 = 8 ((64 t + l) / WN), conflict-free scalar reads.
   constexpr int NT = 32 * WN / 8 / 64;
   constexpr int CW = WN / 8, DRS = 64 / CW;
   static_assert(64 % CW == 0 && NT * DRS == 32, "direct pass covers the strip");
   const int dr0 = lane / CW, dc8 = (lane % CW) * 8;
   const int gj = gc0 + dc8;  // direct pass: this lane's first output column
   auto mpos = [&](int t, int& jj, int& c8) {
-    const int q = t * 64 + lane;
-    jj = q % WN;
-    c8 = (q / WN) * 8;
+    if constexpr (MIR16) {
+      jj = 16 * t + (lane & 15);
+      c8 = 8 * (lane >> 4);
+    } else {
+      const int q = t * 64 + lane;
+      jj = q % WN;
+      c8 = (q / WN) * 8;
+    }
   };
 
   // EPI_POLY's addend E at the direct-pass positions of strip i, as

@@ -5,10 +5,8 @@
 namespace muon {
 
 namespace {
-// 256 x 256 products with row-major operands run 8 waves (two per SIMD, 128 x 64
-// outputs each): 1-3% faster than 4 waves of 128 x 128 on the update, the fused
-// update and the polynomial product; the K-major product measured mixed (1.5%
-// slower on 14336 x 4096 units, 2.7% faster on 4096 x 4096) and keeps 4
+// 256 x 256 products (all row-major here) run 8 waves, two per SIMD, as the
+// bf16 ones do
 template <int T, typename TO, bool SYM, int EPI, bool TRANS = false, int NW = (T == 256 && !TRANS ? 8 : 4)>
 hipError_t go(const GemmArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((gemm_kernel<T, T, f16, TO, SYM, EPI, TRANS, NW>), dim3(a.totalTiles), dim3(64 * NW), 0, s, a);

@@ -124,14 +124,29 @@ def test_lds_plan_in_bounds(BM, NW, ES, TRANS):
     NT, CW = 32 * WN // 8 // 64, WN // 8
     DRS = 64 // CW
     assert 64 % CW == 0 and NT * DRS == 32
-    for lane in range(64):
+    # mirror pass positions: every (strip column, 8-row group) once; 16-bit
+    # strips: the 16-lane groups of one store share the columns (output rows)
+    for mir16 in (True, False):
+        seen = set()
         for t in range(NT):
-            qq = t * 64 + lane
-            jj, c8 = qq % WN, (qq // WN) * 8
-            assert jj < WN and c8 + 7 < 32
-            L = lane & 15
-            off = (c8 + (L >> 2)) * RS16 + (jj - L + 4 * (L & 3)) * 2
-            assert 0 <= off and off + 4 * RS16 + 8 <= 32 * RS16
+            rows_of_store = {}
+            for lane in range(64):
+                if mir16:
+                    jj, c8 = 16 * t + (lane & 15), 8 * (lane >> 4)
+                else:
+                    qq = t * 64 + lane
+                    jj, c8 = qq % WN, (qq // WN) * 8
+                assert jj < WN and c8 + 7 < 32
+                seen.add((jj, c8))
+                rows_of_store.setdefault(jj, set()).add(c8)
+                if mir16:
+                    L = lane & 15
+                    assert jj - L == 16 * t  # a transposed read serves 16 consecutive columns at one c8
+                    off = (c8 + (L >> 2)) * RS16 + (jj - L + 4 * (L & 3)) * 2
+                    assert 0 <= off and off + 4 * RS16 + 8 <= 32 * RS16
+            if mir16:
+                assert all(v == {0, 8, 16, 24} for v in rows_of_store.values()) and len(rows_of_store) == 16
+        assert len(seen) == WN * 4
 
 
 @pytest.mark.parametrize("WTM,WTN", [(4, 4), (4, 2), (2, 2)])
