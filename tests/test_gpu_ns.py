@@ -53,6 +53,19 @@ def test_standard_matches_oracle(shape, dtype):
         assert block_rel_max(O, ref) <= BLOCK_TOL_BF16
 
 
+@pytest.mark.parametrize("shape", [(384, 8192), (8200, 384)])
+def test_kmajor_wave_count_threshold(shape):
+    """A = X X^T is read K-major with K = n, the long side: two waves per
+    SIMD up to K = 8192, one above.  Both sides of the threshold, tall and
+    wide, bf16."""
+    print(f"ns standard K-major threshold {shape}", flush=True)
+    G = _input(*shape, torch.bfloat16, seed=shape[0] * 7919 + shape[1])
+    O = f64(_run(G))
+    ref = cref.orthogonalize(f64(G))
+    assert rel(O, ref) <= TOL[torch.bfloat16], rel(O, ref)
+    assert block_rel_max(O, ref) <= BLOCK_TOL_BF16
+
+
 @pytest.mark.parametrize("shape", TINY)
 def test_standard_tiny_fp32(shape):
     print(f"ns standard tiny fp32 {shape}", flush=True)
