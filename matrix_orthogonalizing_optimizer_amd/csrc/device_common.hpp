@@ -16,6 +16,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// The same address as a global-memory pointer.  Accesses through a generic
+// pointer the compiler cannot trace to a kernel argument (say, one read from
+// a descriptor table) compile to FLAT instructions, which also count in
+// lgkmcnt: an LDS wait after them then waits for those global stores to
+// complete too (the fused update's epilogue did, once per strip: 1-3.5%
+// of that kernel).
+template <typename T> __device__ __forceinline__ __attribute__((address_space(1))) T* as_global(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
 // Storage dtype codes used on the device side.
 enum : int32_t { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
 

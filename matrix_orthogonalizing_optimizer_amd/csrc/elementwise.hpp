@@ -26,12 +26,12 @@ namespace muon {
 // 8 elements of T from p, 16-byte aligned (32 for fp32)
 template <typename T> __device__ __forceinline__ void ld8(const T* p, float (&v)[8]) {
   if constexpr (sizeof(T) == 2) {
-    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    const u32x4 w = __builtin_nontemporal_load(as_global(reinterpret_cast<const u32x4*>(p)));
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = to_f32(__builtin_bit_cast(T, (uint16_t)(w[e >> 1] >> ((e & 1) * 16))));
   } else {
-    const f32x4 lo = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
-    const f32x4 hi = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+    const f32x4 lo = __builtin_nontemporal_load(as_global(reinterpret_cast<const f32x4*>(p)));
+    const f32x4 hi = __builtin_nontemporal_load(as_global(reinterpret_cast<const f32x4*>(p + 4)));
 #pragma unroll
     for (int e = 0; e < 4; ++e) { v[e] = lo[e]; v[e + 4] = hi[e]; }
   }
@@ -44,10 +44,10 @@ template <typename T> __device__ __forceinline__ void st8(T* p, const float (&v)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       w[j] = (uint32_t)bits16(from_f32<T>(v[2 * j])) | ((uint32_t)bits16(from_f32<T>(v[2 * j + 1])) << 16);
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+    __builtin_nontemporal_store(w, as_global(reinterpret_cast<u32x4*>(p)));
   } else {
-    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(p));
-    __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(p + 4));
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, as_global(reinterpret_cast<f32x4*>(p)));
+    __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, as_global(reinterpret_cast<f32x4*>(p + 4)));
   }
 }
 

@@ -159,10 +159,10 @@ template <typename T> __device__ __forceinline__ void store8(T* p, const float (
     u32x4 w;
 #pragma unroll
     for (int j = 0; j < 4; ++j) w[j] = pack2<T>(v[2 * j], v[2 * j + 1]);
-    *reinterpret_cast<u32x4*>(p) = w;
+    *as_global(reinterpret_cast<u32x4*>(p)) = w;
   } else {
-    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    *as_global(reinterpret_cast<f32x4*>(p)) = f32x4{v[0], v[1], v[2], v[3]};
+    *as_global(reinterpret_cast<f32x4*>(p + 4)) = f32x4{v[4], v[5], v[6], v[7]};
   }
 }
 
@@ -235,12 +235,13 @@ __device__ __forceinline__ void final8_vec(TW* w, float* o, const Raw8<TW>& raw,
 template <typename TW>
 __device__ __forceinline__ void final8_tail(TW* w, float* o, const float (&v)[8], int n_valid, float keep,
                                             float step, bool store_only) {
+  auto* wg = as_global(w);
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     if (e < n_valid) {
-      const float x = store_only ? v[e] : to_f32(w[e]) * keep - step * v[e];
-      w[e] = from_f32<TW>(x);
-      if (o) o[e] = v[e];
+      const float x = store_only ? v[e] : to_f32(wg[e]) * keep - step * v[e];
+      wg[e] = from_f32<TW>(x);
+      if (o) as_global(o)[e] = v[e];
     }
   }
 }

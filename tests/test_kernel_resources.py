@@ -71,3 +71,14 @@ def test_buffer_accesses_not_in_waterfall_loops(tmp_path, src):
         window = lines[max(0, i - 4):i]
         assert not any(w.startswith("s_and_saveexec") for w in window), \
             f"{src}: buffer access at line {i} is inside a waterfall loop: {window + [lines[i]]}"
+
+
+@pytest.mark.parametrize("src", ["gemm_bf16.hip", "gemm_f16.hip", "gemm_f32.hip"])
+def test_gemm_kernels_use_no_flat_memory_instructions(tmp_path, src):
+    """Every global access of the GEMM kernels is a buffer or global
+    instruction: a FLAT access also counts in lgkmcnt, so the epilogue's
+    next LDS wait would wait for that global store to complete."""
+    out = tmp_path / (src + ".s")
+    _compile(src, ["-S", "-o", str(out)])
+    flat = [l.strip() for l in out.read_text().splitlines() if l.strip().startswith("flat_")]
+    assert not flat, f"{src}: {len(flat)} FLAT instructions, e.g. {flat[:3]}"
