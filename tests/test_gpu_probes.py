@@ -1,5 +1,6 @@
 """GPU checks of the measurement aids the benchmark reports its kernels
-against: the streaming copy moves every byte (a ragged length included) and
+against: both streaming copies (plain, and through the GEMMs' global -> LDS loads)
+move every byte (a ragged length included) and
 the register-only MFMA loop completes with the FLOP count the header states,
 writing a finite value per workgroup."""
 import pytest
@@ -29,3 +30,15 @@ def test_probe_mfma_runs():
     torch.cuda.synchronize()
     assert flops == 8 * 4 * 16 * 8 * 32768
     assert bool(torch.isfinite(sink).all())
+
+
+def test_probe_copy_lds_moves_every_byte():
+    print("muon_probe_copy_lds 1 MiB + 48 B", flush=True)
+    nbytes = (1 << 20) + 48
+    g = torch.Generator(device="cuda:0").manual_seed(6)
+    src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda:0", generator=g)
+    dst = torch.zeros(nbytes + 16, dtype=torch.uint8, device="cuda:0")
+    mo.muon_probe_copy_lds(src, dst, nbytes)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src)
+    assert int(dst[nbytes:].count_nonzero()) == 0  # nothing past the end
