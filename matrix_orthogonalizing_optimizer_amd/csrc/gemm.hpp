@@ -351,15 +351,17 @@ void gemm_kernel(const GemmArgs a) {
   // XCD c & 7: at any time the 8 XCDs work on neighbouring chunks (mostly one
   // unit, whose operands then stay in the Infinity Cache), and the ~32 tiles an
   // XCD runs at once lie in one chunk (operand bands shared through its L2).
-  // S: 32 upper-triangle tiles (64 for the polynomial product), or two 4-row
-  // groups of a non-symmetric product (measured best of 16..272, re-checked
-  // against 16/64 and 4/16 groups after the copy schedule changed).  The tail short of a full round of 8
-  // chunks is split into 8 contiguous ranges, so the map stays a bijection.
+  // S: 32 upper-triangle tiles for the K-major product, 64 for the row-major
+  // symmetric ones (the polynomial, the Gram chain's m x m products), or two
+  // 4-row groups of a non-symmetric product (measured best of 16..272, and
+  // re-checked against 16/32/64 upper tiles and 4/16 groups as the kernels
+  // changed).  The tail short of a full round of 8 chunks is split into 8
+  // contiguous ranges, so the map stays a bijection.
   int logical;
   {
     const int b = blockIdx.x, tot = a.totalTiles;
     const int xcd = b & 7, loc = b >> 3;
-    const int S = SYM ? (EPI == EPI_POLY ? 64 : 32) : 8 * a.tilesN;
+    const int S = SYM ? (TRANS ? 32 : 64) : 8 * a.tilesN;
     const int full = tot / (8 * S);
     if (loc < full * S) {
       logical = (loc / S) * 8 * S + xcd * S + loc % S;
