@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--workload", default="llama3_8b_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--ns-method", choices=["standard", "gram", "auto"], default=None,
+    p.add_argument("--ns-method", choices=["standard", "gram", "auto", "gram_restart"], default=None,
                    help="override the workload's Newton-Schulz method")
     p.add_argument("--no-probes", action="store_true",
                    help="skip the measured MFMA and copy ceilings")
@@ -76,7 +76,7 @@ def main():
     wl = configs.ALL[args.workload]()
     if args.ns_method:
         wl.method = args.ns_method
-    method = {"standard": 0, "gram": 1, "auto": 2}[wl.method]
+    method = {"standard": 0, "gram": 1, "auto": 2, "gram_restart": 3}[wl.method]
     table = wl.table
 
     # ---- inputs (untimed), resident in HBM
@@ -166,7 +166,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, table, "gram" if method == 1 else "standard")
+        cpu = cpu_baseline(wl, table, {1: "gram", 3: "gram_restart"}.get(method, "standard"))
 
     # muon_step only enqueues: its host time per call against the GPU's time
     # per step (the host had queued all K steps after this long)
@@ -230,13 +230,18 @@ def executed_flops(buckets, steps):
             if steps > 1:
                 add("ns_update_PX", (steps - 1) * rect * f * m)
             add("ns_final_update", rect * f * m)
-        else:  # Gram
-            add("gram_r0", tri * f * n)
+        else:  # Gram (1), or restarted Gram (3): after ceil(steps / 2) steps one
+            # n x m product forms X_r and one Gram product recomputes R; that
+            # step has no Z P, P R, R P products
+            rs = 1 if method == 3 and steps >= 2 else 0
+            add("gram_r0", (1 + rs) * tri * f * n)
             add("gram_p", steps * tri * f * m)
-            if steps > 1:
-                add("gram_q", (steps - 1) * tri * f * m)
-                add("gram_t", (steps - 1) * tri * f * m)
-                add("gram_r", (steps - 1) * tri * f * m)
+            if steps - 1 - rs > 0:
+                add("gram_q", (steps - 1 - rs) * tri * f * m)
+                add("gram_t", (steps - 1 - rs) * tri * f * m)
+                add("gram_r", (steps - 1 - rs) * tri * f * m)
+            if rs:
+                add("ns_update_PX", rect * f * m)
             add("ns_final_update", rect * f * m)
     return out
 

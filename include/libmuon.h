@@ -63,9 +63,23 @@ typedef enum {
  * Gram exactly inside the region, where it also does less work (executed
  * cost with symmetric products: standard steps (3 m^2 n + m^3), Gram
  * 3 m^2 n + (6 steps - 5) m^3, so Gram is cheaper for n/m > 5/3), and the
- * standard method elsewhere.  Plans report the method and compute dtype of
- * every bucket. */
-typedef enum { MUON_NS_STANDARD = 0, MUON_NS_GRAM = 1, MUON_NS_AUTO = 2 } muon_ns_method;
+ * standard method elsewhere.  MUON_NS_GRAM_RESTART is an extension (the
+ * pages describe no restart): the Gram chain with one restart after
+ * ceil(steps / 2) steps (steps >= 2), which forms X_r = Q X_0 explicitly,
+ * recomputes R = X_r X_r^T from it and continues with Q = I, so the fp16
+ * chain's rounding restarts from the rectangular iterate.  A 16-bit unit
+ * with m >= 256 runs it in fp16 at any aspect ratio (at most 0.92e-2 where
+ * the plain fp16 chain reaches 1.9-17e-2 on small and square shapes; the
+ * bucket reports MUON_NS_GRAM_RESTART); a smaller or fp32 unit resolves as
+ * for MUON_NS_GRAM.  It costs one more n x m product and one more
+ * m x m x n Gram product per unit.
+ * Plans report the method and compute dtype of every bucket. */
+typedef enum {
+  MUON_NS_STANDARD = 0,
+  MUON_NS_GRAM = 1,
+  MUON_NS_AUTO = 2,
+  MUON_NS_GRAM_RESTART = 3
+} muon_ns_method;
 
 /* Storage dtype of parameters and gradients.  Momentum and AdamW moments are
  * always fp32. */

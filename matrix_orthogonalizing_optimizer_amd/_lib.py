@@ -18,7 +18,7 @@ MUON_OK = 0
 STATUS = {0: "MUON_OK", -1: "MUON_E_ARG", -2: "MUON_E_SHAPE", -3: "MUON_E_DTYPE",
           -4: "MUON_E_METHOD", -5: "MUON_E_WORKSPACE", -6: "MUON_E_HIP", -7: "MUON_E_PLAN",
           -8: "MUON_E_CAPACITY"}
-MUON_NS_STANDARD, MUON_NS_GRAM, MUON_NS_AUTO = 0, 1, 2
+MUON_NS_STANDARD, MUON_NS_GRAM, MUON_NS_AUTO, MUON_NS_GRAM_RESTART = 0, 1, 2, 3
 MUON_F32, MUON_BF16 = 0, 1
 MUON_KIND_MUON, MUON_KIND_ADAMW = 0, 1
 MUON_SCALE_MOONLIGHT, MUON_SCALE_SPECTRAL, MUON_SCALE_UNIT_RMS = 0, 1, 2

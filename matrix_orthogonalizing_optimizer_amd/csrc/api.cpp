@@ -19,6 +19,8 @@
 // Gram method (DeepSpeed page: iterate on the square Gram matrix R = X X^T):
 //   R = 2^e X0 X0^T / s^2 (power-of-two scaled, fp16 for a bf16 bucket);
 //   P_k = a I + b R + c R^2;  Q <- P_k Q;  R <- P_k R P_k;  O = Q X0 / s.
+//   Restarted chain (an extension): after ceil(steps / 2) steps X_r = Q X0 / s,
+//   R = 2^e X_r X_r^T, Q = I; the remaining steps continue; O = Q X_r.
 //   All of R_k, P_k, Q are polynomials in R_0: symmetric and commuting, so
 //   every m x m product is computed as a symmetric one (upper tiles).
 #include <hip/hip_runtime.h>
@@ -212,13 +214,23 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
   char* R = data + b.off[1];
   char* Tm = data + b.off[2];
   char* PZ[3] = {data + b.off[3], data + b.off[4], data + b.off[5]};
+  // Restarted chain: after `ra` steps X_r = Q X_0 is formed and the chain
+  // starts again from it (R = 2^e X_r X_r^T, Q = I); the final product then
+  // takes X_r.  Yb / bsel: the iterate the current chain started from and
+  // the scale that turns it into X (1 / s for U).
+  const int ra = restart_after(b.method, cp.steps);
+  char* Yb = Y0;
+  int bsel = SEL_INV_S;
   GemmArgs g = sym_args(Y0, b.mp, sy, Y0, b.mp, sy, (int)n, R);
   g.alpha = rs; g.alphaSel = SEL_INV_S2; g.aux = d_aux;
   HIP_TRY(timed(F_GRAM_R0, mm_n, 0.0, st,
                 [&] { return launch_gemm(T, cdt, sdt, true, EPI_SCALE, true, g, st); }));
-  int z = -1;  // buffer holding Z (after the last step: Q)
+  int z = -1;  // buffer holding Z (after the last step: Q); -1: Q = I
   for (int k = 0; k < cp.steps; ++k) {
     const bool last = k + 1 == cp.steps;
+    const bool restart = !last && ra > 0 && k + 1 == ra;
+    // Q feeds a product with the 16-bit iterate after the last step and at a restart
+    const int qdt = (last || restart) ? qdt_last : sdt;
     const float ca = cp.coeffs[3 * k], cb = cp.coeffs[3 * k + 1], cc = cp.coeffs[3 * k + 2];
     int p = 0;
     while (p == z) ++p;
@@ -227,9 +239,9 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
     g.E = R; g.lde = b.mp; g.sE = ss;
     g.alpha = cc / (rs * rs); g.beta = cb / rs; g.gamma = ca;
     HIP_TRY(timed(F_GRAM_P, mmm, 0.0, st, [&] {
-      return launch_gemm(T, sdt, (last && k == 0) ? qdt_last : sdt, true, EPI_POLY, false, g, st);
+      return launch_gemm(T, sdt, z < 0 ? qdt : sdt, true, EPI_POLY, false, g, st);
     }));
-    if (k == 0) {
+    if (z < 0) {
       z = p;  // Z_0 = P_0^T = P_0
     } else {
       int zn = 0;
@@ -239,10 +251,29 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
       // symmetric product (upper tiles + mirror); the last one is Q itself
       g = sym_args(PZ[z], b.mp, ss, PZ[p], b.mp, ss, (int)m, PZ[zn]);
       HIP_TRY(timed(F_GRAM_Q, mmm, 0.0, st,
-                    [&] { return launch_gemm(T, sdt, last ? qdt_last : sdt, true, EPI_SCALE, false, g, st); }));
+                    [&] { return launch_gemm(T, sdt, qdt, true, EPI_SCALE, false, g, st); }));
       z = zn;
     }
-    if (!last) {
+    if (restart) {
+      // X_r = Q X_b, as Y_r = Y_b Q^T (Q symmetric): the standard method's update product
+      char* Yr = data + b.off[6];
+      g = gemm_args(T, cnt, (int)n, (int)m, (int)m, false);
+      g.L = Yb; g.ldl = b.mp; g.sL = sy;
+      g.R = PZ[z]; g.ldr = b.mp; g.sR = ss;
+      g.C = Yr; g.ldc = b.mp; g.sC = sy;
+      g.alpha = 1.f; g.beta = 0.f;
+      g.alphaSel = bsel; g.aux = d_aux;
+      HIP_TRY(timed(F_UPDATE, mm_n, 0.0, st,
+                    [&] { return launch_gemm(T, cdt, cdt, false, EPI_SCALE, false, g, st); }));
+      // R = 2^e X_r X_r^T = 2^e Y_r^T Y_r (Y_r read K-major)
+      g = sym_args(Yr, b.mp, sy, Yr, b.mp, sy, (int)n, R);
+      g.alpha = rs; g.alphaSel = SEL_ONE; g.aux = d_aux;
+      HIP_TRY(timed(F_GRAM_R0, mm_n, 0.0, st,
+                    [&] { return launch_gemm(T, cdt, sdt, true, EPI_SCALE, true, g, st); }));
+      Yb = Yr;
+      bsel = SEL_ONE;
+      z = -1;
+    } else if (!last) {
       // Tm = P R  (R symmetric: its rows serve as R^T; P and R commute, so
       // Tm is symmetric too: upper tiles + mirror)
       g = sym_args(PZ[p], b.mp, ss, R, b.mp, ss, (int)m, Tm);
@@ -254,10 +285,11 @@ muon_status run_chunk(const PlanBucket& b, const UnitDesc* d_desc, float4* d_aux
                     [&] { return launch_gemm(T, sdt, sdt, true, EPI_SCALE, false, g, st); }));
     }
   }
-  // O = Q X0 / s (O^T = Y0 Q^T / s for a tall unit), fused with the update
-  g = final_gemm(Y0, PZ[z]);
+  // O = Q X0 / s (O^T = Y0 Q^T / s for a tall unit; after a restart Q X_r),
+  // fused with the update
+  g = final_gemm(Yb, PZ[z]);
   g.beta = 0.f;
-  g.alphaSel = SEL_INV_S;
+  g.alphaSel = bsel;
   g.aux = d_aux;
   HIP_TRY(timed(F_FINAL, mm_n, elems * 2.0 * pes, st,
                 [&] { return launch_gemm(T, cdt, pdt, false, EPI_FINAL, false, g, st); }));
@@ -533,7 +565,7 @@ static void ns_layout(const PlanBucket& b, size_t& off_aux, size_t& off_part, si
 
 static muon_status ns_bucket(int64_t rows, int64_t cols, int32_t dtype, int32_t method, PlanBucket& b) {
   if (dtype != MUON_F32 && dtype != MUON_BF16) return MUON_E_DTYPE;
-  if (method != MUON_NS_STANDARD && method != MUON_NS_GRAM && method != MUON_NS_AUTO) return MUON_E_METHOD;
+  if (!valid_method(method)) return MUON_E_METHOD;
   if (rows < 0 || cols < 0 || rows > ((int64_t)1 << 30) || cols > ((int64_t)1 << 30)) return MUON_E_SHAPE;
   std::memset(&b, 0, sizeof(b));
   b.m = (int32_t)std::min(rows, cols);

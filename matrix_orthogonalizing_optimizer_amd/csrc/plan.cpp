@@ -35,10 +35,30 @@ static size_t align_ws(size_t x) { return (x + WS_ALIGN - 1) / WS_ALIGN * WS_ALI
 // 512 x 860 and 96 x 300, above the fp32 tolerance of 1e-4).
 bool gram_fp16_ok(int64_t m, int64_t n) { return m >= 512 && n >= 3 * m; }
 
+// The restarted chain (MUON_NS_GRAM_RESTART) serves the 16-bit compute dtype
+// for m >= 256: one restart after ceil(steps / 2) steps keeps the fp16 chain
+// within the bf16 tolerance there (emulated at most 0.92e-2 from 256 x 256
+// to 2048 x 2048, ranks 8 and 64; the emulation matched the kernels to a few
+// percent where both were measured).  Below, rank-64 gradients reach
+// 1.2-2.7e-2 (128 x 128 to 160 x 160), too close to 2e-2 or past it, so
+// such a unit is resolved as a plain Gram request (the fp32 chain), as is
+// any fp32 request.
+constexpr int64_t kRestartMinM = 256;
+
 int32_t resolve_method(int32_t method, int32_t cdtype, int64_t m, int64_t n) {
   if (method == MUON_NS_AUTO) return gram_fp16_ok(m, n) ? MUON_NS_GRAM : MUON_NS_STANDARD;
+  if (method == MUON_NS_GRAM_RESTART && (cdtype == MUON_F32 || m < kRestartMinM)) method = MUON_NS_GRAM;
   if (method == MUON_NS_GRAM && cdtype == MUON_F32 && !gram_fp16_ok(m, n)) return MUON_NS_STANDARD;
   return method;
+}
+
+bool valid_method(int32_t method) {
+  return method == MUON_NS_STANDARD || method == MUON_NS_GRAM || method == MUON_NS_AUTO ||
+         method == MUON_NS_GRAM_RESTART;
+}
+
+int32_t restart_after(int32_t method, int32_t steps) {
+  return method == MUON_NS_GRAM_RESTART && steps >= 2 ? (steps + 1) / 2 : 0;
 }
 
 int32_t resolve_cdtype(int32_t cdtype, int32_t method, int64_t m, int64_t n) {
@@ -55,12 +75,13 @@ bool bucket_addressable(const PlanBucket& b) {
 // Per unit: Y = X^T (n x mp), the transposed copy of the unit kept through the
 // iteration (the symmetric products read it K-major); standard method: Y0,
 // Y1, A, P; Gram: Y0, R, T and three P / Z buffers (m x mp each, fp16 for a
-// bf16 bucket).
+// bf16 bucket); the restarted chain also Yr, the restart's iterate (n x mp).
 size_t per_unit_data_bytes(const PlanBucket& b) {
   const size_t es = (size_t)elem_size(b.cdtype);
   const size_t yb = (size_t)b.n * (size_t)b.mp * es;
   const size_t sb = (size_t)b.m * (size_t)b.mp * es;
   if (b.method == MUON_NS_GRAM) return yb + 5 * sb;
+  if (b.method == MUON_NS_GRAM_RESTART) return 2 * yb + 5 * sb;
   return 2 * yb + 2 * sb;
 }
 
@@ -81,8 +102,9 @@ void bucket_derive(PlanBucket& b, size_t chunk_cap_bytes) {
   size_t o = 0;
   for (int i = 0; i < 8; ++i) b.off[i] = 0;
   b.off[0] = o; o += yb;
-  if (b.method == MUON_NS_GRAM) {
+  if (b.method == MUON_NS_GRAM || b.method == MUON_NS_GRAM_RESTART) {
     for (int i = 1; i < 6; ++i) { b.off[i] = o; o += sb; }
+    if (b.method == MUON_NS_GRAM_RESTART) { b.off[6] = o; o += yb; }
   } else {
     b.off[1] = o; o += yb;
     b.off[2] = o; o += sb;
@@ -96,8 +118,7 @@ muon_status build_plan(const muon_param_shape* table, int32_t n, const muon_plan
   if (n < 0 || (n > 0 && !table)) return MUON_E_ARG;
   muon_plan_options o{MUON_NS_STANDARD, -1};
   if (opts) o = *opts;
-  if (o.ns_method != MUON_NS_STANDARD && o.ns_method != MUON_NS_GRAM && o.ns_method != MUON_NS_AUTO)
-    return MUON_E_METHOD;
+  if (!valid_method(o.ns_method)) return MUON_E_METHOD;
   if (o.ns_dtype != -1 && o.ns_dtype != MUON_F32 && o.ns_dtype != MUON_BF16) return MUON_E_DTYPE;
   P.table.assign(table, table + n);
   P.opts = o;

@@ -27,7 +27,7 @@ struct PlanBucket {
   int32_t tile;          // GEMM tile edge (128 or 256)
   int64_t mp;            // leading dimension of every workspace matrix (round_up(m, 8))
   int32_t km_tiles;      // momentum-kernel workgroups per unit
-  size_t off[8];         // data sub-buffers: standard Y0 Y1 A B; gram Y0 R T PZ0 PZ1 PZ2
+  size_t off[8];         // data sub-buffers: standard Y0 Y1 A B; gram Y0 R T PZ0 PZ1 PZ2 (Yr)
   size_t data_bytes;     // per chunk
 };
 
@@ -58,6 +58,9 @@ bool gram_fp16_ok(int64_t m, int64_t n);  // the fp16 Gram chain meets the bf16 
 int32_t resolve_method(int32_t method, int32_t cdtype, int64_t m, int64_t n);
 // the compute dtype it runs in (a bf16 Gram unit outside gram_fp16_ok -> fp32)
 int32_t resolve_cdtype(int32_t cdtype, int32_t method, int64_t m, int64_t n);
+bool valid_method(int32_t method);  // a muon_ns_method value
+// steps after which the restarted Gram chain restarts (0: no restart)
+int32_t restart_after(int32_t method, int32_t steps);
 size_t per_unit_data_bytes(const PlanBucket& b);
 
 muon_status build_plan(const muon_param_shape* table, int32_t n, const muon_plan_options* opts,

@@ -96,11 +96,11 @@ def orthogonalize(G, steps: int = 5, coeffs: Optional[Sequence] = None, method: 
         if c.shape != (steps, 3):
             raise ValueError("coeffs must be (3,) or (steps, 3)")
         c = np.ascontiguousarray(c)
-    if method not in ("standard", "gram"):
+    if method not in ("standard", "gram", "gram_restart"):
         raise ValueError(f"unknown ns method {method!r}")
     O = np.empty_like(G)
     st = lib().ref_orthogonalize(_p(G), rows, cols, steps, _p(c) if c is not None else None,
-                                 {"standard": 0, "gram": 1}[method], _p(O))
+                                 {"standard": 0, "gram": 1, "gram_restart": 3}[method], _p(O))
     if st != 0:
         raise ValueError("ref_orthogonalize rejected its arguments")
     return O

@@ -109,10 +109,12 @@ Mat ns_standard(Mat X, int64_t m, int64_t n, const double* coeffs, int steps) {
 // [DeepSpeed] Gram variant: iterate on the square R = X X^T.  The page states
 // only that; the reading taken is the exact rewrite of the standard step:
 // P_k = a I + b R_k + c R_k R_k, X_{k+1} = P_k X_k, so R_{k+1} = P_k R_k P_k
-// and the result is Q X_0 with Q = P_{N-1} ... P_0.
-Mat ns_gram(const Mat& X, int64_t m, int64_t n, const double* coeffs, int steps) {
-  const Mat Xt = transpose(X, m, n);
-  Mat R = matmul(X, Xt, m, n, m);
+// and the result is Q X_0 with Q = P_{N-1} ... P_0.  restart > 0: after that
+// many steps the chain restarts once (an extension; the pages have none):
+// X_r = Q X_0 is formed, R = X_r X_r^T recomputed and Q reset to I.
+Mat ns_gram(const Mat& X0, int64_t m, int64_t n, const double* coeffs, int steps, int restart) {
+  Mat X = X0;
+  Mat R = matmul(X, transpose(X, m, n), m, n, m);
   Mat Q = identity(m);
   for (int k = 0; k < steps; ++k) {
     const double a = coeffs[3 * k], b = coeffs[3 * k + 1], c = coeffs[3 * k + 2];
@@ -124,7 +126,14 @@ Mat ns_gram(const Mat& X, int64_t m, int64_t n, const double* coeffs, int steps)
         P[e] = (i == j ? a : 0.0) + b * R[e] + c * RR[e];
       }
     Q = matmul(P, Q, m, m, m);
-    if (k + 1 < steps) R = matmul(matmul(P, R, m, m, m), P, m, m, m);
+    if (k + 1 == steps) break;
+    if (restart > 0 && k + 1 == restart) {
+      X = matmul(Q, X, m, m, n);
+      R = matmul(X, transpose(X, m, n), m, n, m);
+      Q = identity(m);
+    } else {
+      R = matmul(matmul(P, R, m, m, m), P, m, m, m);
+    }
   }
   return matmul(Q, X, m, m, n);
 }
@@ -154,10 +163,11 @@ void ref_momentum(double* M, const double* G, int64_t count, double mu, int32_t 
 // (G G^T)^{-1/2} G = G (G^T G)^{-1/2}), G is divided by its Frobenius norm
 // ("Newton-Schulz Iteration"; a zero matrix gives O = 0), then `steps`
 // iterations with coeffs (steps x 3, or null for the quintic every step).
-// method 0 = standard, 1 = Gram.  Returns 0, or -1 for bad arguments.
+// method 0 = standard, 1 = Gram, 3 = Gram restarted after ceil(steps / 2)
+// steps (steps >= 2).  Returns 0, or -1 for bad arguments.
 int32_t ref_orthogonalize(const double* G, int64_t rows, int64_t cols, int32_t steps, const double* coeffs,
                           int32_t method, double* O) {
-  if (rows < 0 || cols < 0 || steps < 0 || (method != 0 && method != 1)) return -1;
+  if (rows < 0 || cols < 0 || steps < 0 || (method != 0 && method != 1 && method != 3)) return -1;
   const size_t cnt = (size_t)(rows * cols);
   if (cnt == 0) return 0;
   std::vector<double> sched((size_t)steps * 3);
@@ -175,7 +185,8 @@ int32_t ref_orthogonalize(const double* G, int64_t rows, int64_t cols, int32_t s
     return 0;
   }
   for (size_t e = 0; e < cnt; ++e) X[e] /= s;
-  X = method == 0 ? ns_standard(X, m, n, sched.data(), steps) : ns_gram(X, m, n, sched.data(), steps);
+  const int restart = method == 3 && steps >= 2 ? (steps + 1) / 2 : 0;
+  X = method == 0 ? ns_standard(X, m, n, sched.data(), steps) : ns_gram(X, m, n, sched.data(), steps, restart);
   if (tall) X = transpose(X, m, n);
   std::memcpy(O, X.data(), cnt * sizeof(double));
   return 0;
@@ -267,12 +278,14 @@ int64_t ref_plan(const int64_t* table, int32_t n, int32_t method, int32_t ns_dty
     // An explicit Gram request outside it runs its chain in fp32 when the
     // requested compute dtype is bf16 (code 1 -> 0), and runs the standard
     // method when it is fp32 (the fp32 chain there is above the fp32
-    // tolerance)
+    // tolerance).  The restarted chain (3) stays 3 for a bf16 compute dtype
+    // when m >= 256 and is taken as a Gram request (1) otherwise.
     const bool fp16_ok = m >= 512 && nn >= 3 * m;
     int64_t cdt = ns_dtype < 0 ? pdt : ns_dtype;
     int64_t meth = method;
+    if (method == 3 && (cdt == 0 || m < 256)) meth = 1;
     if (method == 2) meth = fp16_ok ? 1 : 0;
-    else if (method == 1 && cdt == 0 && !fp16_ok) meth = 0;
+    else if (meth == 1 && cdt == 0 && !fp16_ok) meth = 0;
     if (meth == 1 && cdt == 1 && !fp16_ok) cdt = 0;
     const std::vector<int64_t> key = {m, nn, u.tall, pdt, cdt, meth};
     size_t b = 0;

@@ -116,24 +116,44 @@ def ns_standard(X: np.ndarray, schedule) -> np.ndarray:
     return X
 
 
-def ns_gram(X: np.ndarray, schedule) -> np.ndarray:
+def ns_gram(X: np.ndarray, schedule, restart_after: int = 0, dtype=np.float64) -> np.ndarray:
     """Gram variant ([DeepSpeed]: iterate on the small square Gram matrix
     R = X X^T instead of the rectangular X).  The page describes only that;
     the reading taken is the exact-arithmetic rewrite of ``ns_standard``:
     with P_k = a I + b R_k + c R_k^2 one has X_{k+1} = P_k X_k, so
-    R_{k+1} = P_k R_k P_k and X_N = (P_{N-1} ... P_0) X_0 = Q X_0."""
-    X = np.asarray(X, dtype=np.float64)
+    R_{k+1} = P_k R_k P_k and X_N = (P_{N-1} ... P_0) X_0 = Q X_0.
+
+    ``restart_after`` = r > 0 restarts the chain once, after r steps (an
+    extension; the pages describe no restart): X_r = Q X_0 is formed, R is
+    recomputed as X_r X_r^T and Q starts again from I, so the result is
+    Q' X_r.  In exact arithmetic that changes nothing; in rounded arithmetic
+    the chain's error restarts from the rectangular iterate.  ``dtype``: the
+    arithmetic of the chain (fp64; a pin rounds it to fp32 to see the
+    restart)."""
+    X = np.asarray(X, dtype=np.float64).astype(dtype)
     m = X.shape[0]
-    I = np.eye(m)
+    I = np.eye(m, dtype=dtype)
     R = X @ X.T
     Q = I.copy()
     steps = len(schedule)
     for k, (a, b, c) in enumerate(schedule):
+        a, b, c = dtype(a), dtype(b), dtype(c)
         P = a * I + b * R + c * (R @ R)
         Q = P @ Q
         if k < steps - 1:
-            R = P @ R @ P
-    return Q @ X
+            if restart_after > 0 and k + 1 == restart_after:
+                X = Q @ X
+                R = X @ X.T
+                Q = I.copy()
+            else:
+                R = P @ R @ P
+    return (Q @ X).astype(np.float64)
+
+
+def restart_step(steps: int) -> int:
+    """Where the restarted Gram chain restarts: after ceil(steps / 2) steps
+    when there are at least two (the reading taken for the extension)."""
+    return (steps + 1) // 2 if steps >= 2 else 0
 
 
 def orthogonalize(G: np.ndarray, steps: int = DEFAULT_STEPS, coeffs=None,
@@ -160,6 +180,8 @@ def orthogonalize(G: np.ndarray, steps: int = DEFAULT_STEPS, coeffs=None,
         X = ns_standard(X, sched)
     elif method == "gram":
         X = ns_gram(X, sched)
+    elif method == "gram_restart":
+        X = ns_gram(X, sched, restart_after=restart_step(len(sched)))
     else:
         raise ValueError(f"unknown ns method {method!r}")
     return X.T.copy() if tall else X
@@ -296,9 +318,14 @@ def resolve_method(method: int, dt: int, m: int, n: int) -> int:
     the standard method otherwise.  An explicit Gram request (1) for the
     fp32 compute dtype (code 0) outside that region is served by the
     standard method: the fp32 Gram chain there measured above the fp32
-    tolerance (1.1-1.8e-4 on 768 x 768, 512 x 860, 96 x 300)."""
+    tolerance (1.1-1.8e-4 on 768 x 768, 512 x 860, 96 x 300).  The
+    restarted Gram chain (3) is kept for the 16-bit compute dtype when
+    m >= 256 (there its restart keeps the fp16 chain within the bf16
+    tolerance) and resolved as a Gram request (1) otherwise."""
     if method == 2:
         return 1 if gram_fp16_ok(m, n) else 0
+    if method == 3 and (dt == DT_F32 or m < 256):
+        method = 1
     if method == 1 and dt == DT_F32 and not gram_fp16_ok(m, n):
         return 0
     return method

@@ -128,6 +128,35 @@ def test_auto_method_resolution():
     assert all(b[4] == 1 for b in mo.muon_plan_buckets(mo.muon_plan_create(table, mo.MUON_NS_AUTO)))
 
 
+def test_restarted_gram_resolution():
+    """The restarted Gram chain keeps the 16-bit compute dtype for m >= 256
+    at any aspect ratio (the restart holds the fp16 chain within tolerance);
+    a smaller unit, and any fp32 request, is taken as a plain Gram request;
+    its workspace holds one more n x m copy."""
+    _lib_or_skip()
+    table = [(0, 1, 256, 1024, 0, 0), (0, 1, 768, 768, 0, 0), (0, 1, 768, 3072, 0, 0),
+             (0, 1, 255, 300, 0, 0), (0, 1, 64, 200, 0, 0), (0, 0, 256, 512, 0, 0), (0, 0, 512, 1536, 0, 0)]
+    b = mo.muon_plan_buckets(mo.muon_plan_create(table, mo.MUON_NS_GRAM_RESTART))
+    assert [x[5] for x in b] == [3, 3, 3, 1, 1, 0, 1]
+    assert [x[4] for x in b] == [1, 1, 1, 0, 0, 0, 0]
+    b = mo.muon_plan_buckets(mo.muon_plan_create(table, mo.MUON_NS_GRAM_RESTART, 1))
+    assert [x[5] for x in b] == [3, 3, 3, 1, 1, 3, 3] and [x[4] for x in b] == [1, 1, 1, 0, 0, 1, 1]
+    b = mo.muon_plan_buckets(mo.muon_plan_create(table, mo.MUON_NS_GRAM_RESTART, 0))
+    assert [x[5] for x in b] == [0, 0, 1, 0, 0, 0, 1] and [x[4] for x in b] == [0] * 7
+    for shape in ((256, 1024), (768, 768), (3072, 768)):
+        r = mo.ns_orthogonalize_workspace_bytes(*shape, 1, mo.MUON_NS_GRAM_RESTART)
+        g = mo.ns_orthogonalize_workspace_bytes(*shape, 1, mo.MUON_NS_GRAM)
+        if min(shape) >= 512 and max(shape) >= 3 * min(shape):
+            # Gram in fp16 too: exactly one more n x mp 16-bit copy (with the
+            # layout's alignment slack)
+            extra = max(shape) * ((min(shape) + 7) // 8 * 8) * 2
+            assert extra <= r - g <= extra + 256
+        else:
+            assert r > 0
+    assert (mo.ns_orthogonalize_workspace_bytes(256, 1024, 0, mo.MUON_NS_GRAM_RESTART)
+            == mo.ns_orthogonalize_workspace_bytes(256, 1024, 0, mo.MUON_NS_STANDARD))
+
+
 def test_explicit_gram_outside_fp16_region():
     """An explicit Gram request outside m >= 512, n >= 3m: a bf16 unit runs
     the Gram chain in fp32 (compute dtype 0), an fp32 unit the standard
@@ -208,7 +237,10 @@ def test_ns_orthogonalize_validation():
     assert mo.ns_orthogonalize_workspace_bytes(96, 64, 1) == nb  # tall uses the same shape
     f = L.ns_orthogonalize
     assert f(0x1000, 64, 96, 96, 9, 5, None, 0, 0x10000, nb, None) == -3
-    assert f(0x1000, 64, 96, 96, 1, 5, None, 3, 0x10000, nb, None) == -4
+    assert f(0x1000, 64, 96, 96, 1, 5, None, 4, 0x10000, nb, None) == -4
+    assert f(0x1000, 64, 96, 96, 1, 5, None, -1, 0x10000, nb, None) == -4
+    # the restarted Gram chain needs more than the standard workspace
+    assert f(0x1000, 64, 96, 96, 1, 5, None, 3, 0x10000, nb, None) == -5
     assert f(0x1000, 64, 96, 90, 1, 5, None, 0, 0x10000, nb, None) == -2
     assert f(0x1000, 64, 96, 96, 1, 0, None, 0, 0x10000, nb, None) == -1
     assert f(None, 64, 96, 96, 1, 5, None, 0, 0x10000, nb, None) == -1
@@ -323,7 +355,7 @@ def test_plan_random_tables_match_both_references(seed):
     import numpy as np
     rng = np.random.default_rng(1000 + seed)
     table = _random_table(rng, int(rng.integers(1, 25)))
-    for method in (0, 1, 2):
+    for method in (0, 1, 2, 3):
         for ns_dtype in (-1, 0, 1):
             plan = mo.muon_plan_create(table, method, ns_dtype)
             units, keys, members = oracle.plan_buckets(table, method, ns_dtype)

@@ -68,23 +68,35 @@ def _brute_executed(buckets, steps):
                 add("ns_update_PX", (steps - 1) * count * full * tile * m)
             add("ns_final_update", count * full * tile * m)
         else:
+            # walk the launch sequence of the Gram chain step by step
+            ra = (steps + 1) // 2 if method == 3 and steps >= 2 else 0
             add("gram_r0", count * upper * tile * n)
-            add("gram_p", steps * count * upper * tile * m)
-            for k in ("gram_q", "gram_t", "gram_r"):
-                if steps > 1:
-                    add(k, (steps - 1) * count * upper * tile * m)
+            have_q = False
+            for k in range(steps):
+                last = k == steps - 1
+                add("gram_p", count * upper * tile * m)
+                if have_q:
+                    add("gram_q", count * upper * tile * m)
+                have_q = True
+                if not last and ra and k + 1 == ra:
+                    add("ns_update_PX", count * full * tile * m)
+                    add("gram_r0", count * upper * tile * n)
+                    have_q = False
+                elif not last:
+                    add("gram_t", count * upper * tile * m)
+                    add("gram_r", count * upper * tile * m)
             add("ns_final_update", count * full * tile * m)
     return out
 
 
 @pytest.mark.parametrize("name", sorted(configs.ALL))
-@pytest.mark.parametrize("method", [0, 1, 2])
+@pytest.mark.parametrize("method", [0, 1, 2, 3])
 def test_executed_flops_brute_force(name, method):
     mo = pytest.importorskip("matrix_orthogonalizing_optimizer_amd")
     b = _bench()
     wl = configs.ALL[name]()
     buckets = mo.muon_plan_buckets(mo.muon_plan_create(wl.table, method))
-    for steps in (1, 5):
+    for steps in (1, 2, 5, 10):
         assert b.executed_flops(buckets, steps) == _brute_executed(buckets, steps)
 
 

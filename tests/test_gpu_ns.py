@@ -113,6 +113,50 @@ def test_gram_matches_oracle(shape, dtype):
         assert rel(O, ref) <= TOL[dtype], (rank, rel(O, ref))
 
 
+# Restarted Gram chain (an extension): fp16 for every 16-bit unit with
+# m >= 256, small, square and ragged ones included, where the plain fp16
+# chain misses the tolerance (emulated 1.9-17e-2); m < 256 takes the fp32
+# Gram chain (255 x 300, 129 x 1000, 96 x 300, 64 x 200).  bf16 against the
+# reference's restarted chain (equal to the standard result in fp64), with
+# the per-block bound.
+RESTART_SHAPES = [(256, 512), (512, 256), (256, 256), (300, 1100), (384, 384), (768, 768), (512, 860),
+                  (1024, 1024), (1408, 2048), (768, 3072), (3072, 768),
+                  (255, 300), (129, 1000), (96, 300), (64, 200)]
+
+
+@pytest.mark.parametrize("shape", RESTART_SHAPES)
+def test_gram_restart_matches_oracle(shape):
+    print(f"ns gram restart {shape}", flush=True)
+    for rank in (8, 64):
+        G = _input(*shape, torch.bfloat16, seed=shape[0] * 37 + shape[1] + rank, rank=rank)
+        O = f64(_run(G, method=mo.MUON_NS_GRAM_RESTART))
+        ref = cref.orthogonalize(f64(G), method="gram_restart")
+        e, eb = rel(O, ref), block_rel_max(O, ref)
+        print(f"  rank {rank}: rel {e:.3e} block {eb:.3e}", flush=True)
+        assert e <= TOL[torch.bfloat16] and eb <= BLOCK_TOL_BF16, (rank, e, eb)
+
+
+@pytest.mark.parametrize("steps", [2, 3, 10])
+def test_gram_restart_step_counts(steps):
+    """The restart sits after ceil(steps / 2) steps: 2, 3 and 10 steps
+    (the ten-step hybrid schedule) against the reference."""
+    print(f"ns gram restart steps={steps}", flush=True)
+    coeffs = mo.muon_ns_coefficients(mo.MUON_COEFF_HYBRID, steps) if steps == 10 else None
+    G = _input(384, 1000, torch.bfloat16, seed=steps + 5)
+    O = f64(_run(G, method=mo.MUON_NS_GRAM_RESTART, steps=steps, coeffs=coeffs))
+    ref = cref.orthogonalize(f64(G), steps=steps, coeffs=coeffs, method="gram_restart")
+    assert rel(O, ref) <= TOL[torch.bfloat16], rel(O, ref)
+
+
+@pytest.mark.parametrize("shape", [(256, 1024), (768, 3072)])
+def test_gram_restart_fp32_resolves_as_gram(shape):
+    print(f"ns gram restart fp32 {shape}", flush=True)
+    G = _input(*shape, torch.float32, seed=shape[0] + 1)
+    O = f64(_run(G, method=mo.MUON_NS_GRAM_RESTART))
+    ref = cref.orthogonalize(f64(G), method="standard")
+    assert rel(O, ref) <= TOL[torch.float32], rel(O, ref)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_coefficient_schedule_and_steps(dtype):
     G = _input(200, 330, dtype, seed=5)

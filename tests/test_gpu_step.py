@@ -416,6 +416,38 @@ def test_nan_filled_workspace(which):
             assert torch.isfinite(x.float()).all()
 
 
+def test_restarted_gram_step():
+    """One muon_step with the restarted Gram chain over wide, tall, square and
+    small units (the fp16 chain with its restart for m >= 256, the fp32
+    Gram chain for 96 x 300) and an fp32 unit (resolved as a Gram request:
+    the standard method outside m >= 512, n >= 3m): O, W and M of every unit
+    against the numpy reference."""
+    print("muon_step ns_method=gram_restart", flush=True)
+    d = dev()
+    table = [(0, 1, 512, 1536, 0, 0), (0, 1, 1536, 512, 0, 0), (0, 1, 256, 1024, 0, 0), (0, 1, 640, 640, 0, 0),
+             (0, 1, 96, 300, 0, 0), (0, 0, 300, 700, 0, 0)]
+    wl = configs.Workload("gram_restart", table, [f"p{i}" for i in range(6)], rank=8, hp=configs._hp())
+    P, M, EA, ES = _state(wl, d)
+    G = gen.make_grads(wl, 0, "cpu")
+    W0 = [f64(p) for p in P]
+    outs = [torch.zeros(r[2], r[3], dtype=torch.float32, device=d) for r in table]
+    run = StepRunner(table, method=mo.MUON_NS_GRAM_RESTART, device=d)
+    b = mo.muon_plan_buckets(run.plan)
+    assert [(x[4], x[5]) for x in b] == [(1, 3), (1, 3), (1, 3), (1, 3), (0, 1), (0, 0)]
+    run.step(P, [g.to(d) for g in G], M, EA, ES, hp_from(wl.hp), update_outs=outs)
+    torch.cuda.synchronize()
+    ref = oracle.muon_step(table, W0, [f64(g) for g in G], [np.zeros((r[2], r[3])) for r in table],
+                           [None] * 6, [None] * 6, _oracle_hp(wl.hp), method="gram_restart", want_updates=True)
+    for i, r in enumerate(table):
+        tol = 1e-4 if r[1] == 0 else 2e-2
+        e = rel(f64(outs[i]), ref["O"][i])
+        print(f"  {r[2]}x{r[3]} dtype {r[1]}: O rel err {e:.3e}", flush=True)
+        assert e <= tol, (i, e)
+        w_ref = ref["W"][i] if r[1] == 0 else stored(ref["W"][i], torch.bfloat16)
+        assert rel(f64(P[i]) - W0[i], w_ref - W0[i]) <= tol
+        assert rel(f64(M[i]), ref["M"][i]) <= 1e-6
+
+
 def test_explicit_gram_step_every_precision_path():
     """One muon_step with ns_method gram over units that take each of its
     resolutions: the fp16 chain (512 x 1536 wide and tall), the fp32 chain of

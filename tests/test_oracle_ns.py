@@ -1,8 +1,8 @@
 """Pins of the oracle's orthogonalization against what the mathematics fixes:
 the SVD closed form of the iteration, hand-reduced and rank-1 cases, the exact
 msign limit of convergent coefficient sets, scalar fixed points of g,
-symmetries, the Gram rewrite and the singular-value band.  Every test runs on
-both references: the numpy one and the plain C++ one (oracle/muon_ref.cpp),
+symmetries, the Gram rewrite (with and without its restart) and the
+singular-value band.  Every test runs on both references: the numpy one and the plain C++ one (oracle/muon_ref.cpp),
 which share no code."""
 import json
 import math
@@ -49,7 +49,7 @@ def test_matches_svd_closed_form(shape, impl):
     assert rel(O, closed_form(G)) < 1e-12
 
 
-@pytest.mark.parametrize("method", ["standard", "gram"])
+@pytest.mark.parametrize("method", ["standard", "gram", "gram_restart"])
 def test_lowrank_closed_form(method, impl):
     # a gradient of the workload kind: geometric spectrum 1..1e-3 plus noise
     r = rng(7)
@@ -127,6 +127,47 @@ def test_gram_equals_standard(impl):
         a = impl.orthogonalize(G, method="standard")
         b = impl.orthogonalize(G, method="gram")
         assert rel(b, a) < 1e-11
+
+
+def test_restarted_gram_equals_standard(impl):
+    """The restart changes nothing in exact arithmetic: X_r = Q X_0 is the
+    standard iterate after r steps and R = X_r X_r^T its Gram matrix.  Any
+    step count (the restart sits after ceil(steps / 2) of them), per-step
+    coefficients, tall and wide inputs."""
+    r = rng(15)
+    for shape, steps in [((12, 40), 5), ((40, 12), 5), ((16, 16), 2), ((9, 30), 3), ((20, 33), 10)]:
+        G = r.standard_normal(shape)
+        coeffs = [(3.4445 - 0.1 * k, -4.7750 + 0.05 * k, 2.0315) for k in range(steps)]
+        a = impl.orthogonalize(G, steps=steps, coeffs=coeffs, method="standard")
+        b = impl.orthogonalize(G, steps=steps, coeffs=coeffs, method="gram_restart")
+        assert rel(b, a) < 1e-11
+
+
+def test_restart_step():
+    assert [oracle.restart_step(s) for s in (0, 1, 2, 3, 5, 10)] == [0, 0, 1, 2, 3, 5]
+
+
+@pytest.mark.parametrize("shape", [(96, 128), (128, 128)])
+def test_restart_cuts_rounded_chain_error(shape):
+    """What the restart is for, seen in rounded arithmetic (numpy reference,
+    chain in fp32): restarting from the rectangular iterate where the
+    library does (after three of the five steps) brings the chain at least
+    4x closer to the fp64 standard result than the plain chain.  A restart
+    that never happens, or one that loses Q, fails this."""
+    m, n = shape
+    r = rng(m + n)
+    U, _ = np.linalg.qr(r.standard_normal((m, m)))
+    V, _ = np.linalg.qr(r.standard_normal((n, m)))
+    G = (U * np.geomspace(1.0, 1e-3, m)) @ V.T
+    X = G / np.linalg.norm(G)
+    ref = oracle.ns_standard(X, [QUINTIC] * 5)
+    plain = oracle.ns_gram(X, [QUINTIC] * 5, dtype=np.float32)
+    restarted = oracle.ns_gram(X, [QUINTIC] * 5, restart_after=oracle.restart_step(5), dtype=np.float32)
+    e_plain, e_rst = rel(plain, ref), rel(restarted, ref)
+    assert 1e-5 < e_plain < 1e-3
+    assert e_rst * 4 < e_plain
+    # and in fp64 both are the standard result
+    assert rel(oracle.ns_gram(X, [QUINTIC] * 5, restart_after=2), ref) < 1e-12
 
 
 def test_per_step_schedule_matches_constant(impl):
