@@ -92,7 +92,7 @@ int run_math(int threads) {
   for (const auto& s : shapes) {
     const int64_t r = s[0], c = s[1];
     const size_t cnt = (size_t)(r * c);
-    for (int method = 0; method < 2; ++method) {
+    for (int method : {0, 1, 3}) {
       for (int steps = 0; steps <= 6; steps += 3) {
         const std::vector<double> G = fill(cnt);
         std::vector<double> coeffs = fill((size_t)steps * 3 + 1);

@@ -107,7 +107,7 @@ def _compare(exes, cases):
 @pytest.mark.parametrize("name", sorted(configs.ALL))
 def test_workload_plans_agree_under_sanitizers(exes, name):
     table = configs.ALL[name]().table
-    _compare(exes, [(table, method, nsd) for method in (0, 1, 2) for nsd in (-1, 0, 1)])
+    _compare(exes, [(table, method, nsd) for method in (0, 1, 2, 3) for nsd in (-1, 0, 1)])
 
 
 def test_random_tables_agree_under_sanitizers(exes):
@@ -124,7 +124,7 @@ def test_random_tables_agree_under_sanitizers(exes):
                 split = rng.choice([h for h in (1, 2, 4, 8, 16, 64, 128) if rows % h == 0] or [0])
             sd = rng.choice([0, 0, 0, 5, 4096])
             table.append((kind, dt, rows, cols, split, sd))
-        cases.append((table, rng.randint(0, 2), rng.choice([-1, 0, 1])))
+        cases.append((table, rng.randint(0, 3), rng.choice([-1, 0, 1])))
     _compare(exes, cases)
 
 
