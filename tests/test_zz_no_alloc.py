@@ -33,7 +33,7 @@ def _noalloc(X, steps=5, method=0):
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_noalloc_matches_workspace_entry_point(dtype):
     d = dev()
-    for shape, method in (((1024, 3000), 0), ((300, 700), 0), ((2048, 512), 1)):
+    for shape, method in (((1024, 3000), 0), ((300, 700), 0), ((2048, 512), 1), ((768, 1536), 3)):
         print(f"ns_orthogonalize_noalloc {shape} {dtype} method {method}", flush=True)
         G = gen.lowrank_gradient(*shape, 8, shape[0] + shape[1], "cpu", torch.float64).to(dtype)
         a = G.to(d).contiguous()
