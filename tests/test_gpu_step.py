@@ -379,14 +379,14 @@ def test_ragged_unaligned_buffers(pdt):
     assert rel(f64(P[2]) - W0[2], w_ref - W0[2]) <= tol
 
 
-def _run_with_workspace(table, wl, fill_byte, device):
+def _run_with_workspace(table, wl, fill_byte, device, method=0):
     """One step from fixed inputs with the workspace pre-filled with a byte
     pattern; returns every output on the host."""
     P, M, EA, ES = _state(wl, device)
     G = [g.to(device) for g in gen.make_grads(wl, 0, "cpu")]
     O = [torch.zeros(r[2], r[3], dtype=torch.float32, device=device) if r[0] == 0 else None
          for r in table]
-    run = StepRunner(table, device=device)
+    run = StepRunner(table, method=method, device=device)
     run.ws.fill_(fill_byte)
     run.step(P, G, M, EA, ES, hp_from(wl.hp), update_outs=O)
     torch.cuda.synchronize()
@@ -394,22 +394,24 @@ def _run_with_workspace(table, wl, fill_byte, device):
     return host(P) + host(M) + host(EA) + host(ES) + host(O)
 
 
-@pytest.mark.parametrize("which", ["gpt2_small", "ragged"])
-def test_nan_filled_workspace(which):
+@pytest.mark.parametrize("which,method", [("gpt2_small", 0), ("ragged", 0), ("ragged", 1), ("ragged", 3)])
+def test_nan_filled_workspace(which, method):
     """Every GEMM reads whole 16-byte pieces and relies on the zero padding of
     the working copies being written by the kernels themselves.  A workspace
     filled with 0xFF bytes (NaN in bf16 and fp32) before the step must give
-    bit-identical results to a zero-filled one."""
-    print(f"muon_step with a NaN-filled workspace: {which}", flush=True)
+    bit-identical results to a zero-filled one: the standard method, the Gram
+    chain (fp16, fp32 and the standard method for fp32 units) and the
+    restarted chain, whose restart iterate X_r is one more working copy."""
+    print(f"muon_step with a NaN-filled workspace: {which}, method {method}", flush=True)
     d = dev()
     if which == "gpt2_small":
         wl = configs.gpt2_small()
     else:
         table = [(0, 1, 300, 701, 0, 0), (0, 1, 701, 300, 0, 0), (0, 1, 200, 130, 0, 0),
-                 (0, 0, 77, 190, 0, 0), (1, 1, 1, 1001, 0, 0)]
-        wl = configs.Workload("ragged", table, [f"p{i}" for i in range(5)], rank=8, hp=configs._hp())
-    a = _run_with_workspace(wl.table, wl, 0, d)
-    b = _run_with_workspace(wl.table, wl, 0xFF, d)
+                 (0, 0, 77, 190, 0, 0), (1, 1, 1, 1001, 0, 0), (0, 1, 514, 1550, 0, 0)]
+        wl = configs.Workload("ragged", table, [f"p{i}" for i in range(6)], rank=8, hp=configs._hp())
+    a = _run_with_workspace(wl.table, wl, 0, d, method)
+    b = _run_with_workspace(wl.table, wl, 0xFF, d, method)
     for x, y in zip(a, b):
         if x is not None:
             assert torch.equal(x, y)
