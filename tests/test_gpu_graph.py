@@ -14,8 +14,11 @@ mo = pytest.importorskip("matrix_orthogonalizing_optimizer_amd")
 pytestmark = pytest.mark.gpu
 
 
-def test_muon_step_graph_replays_match_eager():
-    print("muon_step under graph capture", flush=True)
+@pytest.mark.parametrize("method", [0, 3])
+def test_muon_step_graph_replays_match_eager(method):
+    """Standard method, and the restarted Gram chain (its restart is host
+    orchestration of the same kernels)."""
+    print(f"muon_step under graph capture, method {method}", flush=True)
     d = dev()
     table = [(0, 1, 512, 1536, 0, 0), (0, 1, 1536, 512, 0, 0), (0, 1, 768, 768, 256, 0),
              (0, 0, 300, 701, 0, 0), (1, 1, 1, 1001, 0, 0), (1, 1, 64, 256, 0, 0)]
@@ -23,7 +26,7 @@ def test_muon_step_graph_replays_match_eager():
     P0, M0, EA0, ES0 = gen.make_state(wl, "cpu")
     G = [g.to(d) for g in gen.make_grads(wl, 0, "cpu")]
     to = lambda xs: [None if x is None else x.to(d) for x in xs]
-    run = StepRunner(table, device=d)
+    run = StepRunner(table, method=method, device=d)
     hp = hp_from(wl.hp)
     # eager
     P, M, EA, ES = to(P0), to(M0), to(EA0), to(ES0)
