@@ -227,3 +227,34 @@ def test_sign_symmetry(shape):
     assert np.all(diff <= _ulp_bf16(a))
     a, b = f64(_run(G)), f64(_run(-G))
     assert rel(b, -a) <= 1e-2, rel(b, -a)
+
+
+def _random_cases():
+    """Seeded random shapes and methods: bf16 with min side >= 128 (the
+    workload generator's inputs; smaller sides are covered above with
+    well-conditioned inputs), fp32 from 1 to 700 on a side."""
+    r = np.random.default_rng(20261203)
+    cases = []
+    for i in range(12):
+        if i < 8:
+            a, b = (int(round(float(np.exp(r.uniform(np.log(128), np.log(1100)))))) for _ in range(2))
+            dtype = torch.bfloat16
+        else:
+            a, b = int(r.integers(1, 701)), int(r.integers(1, 701))
+            dtype = torch.float32
+        cases.append(((a, b), int(r.choice([0, 1, 3])), dtype))
+    return cases
+
+
+@pytest.mark.parametrize("shape,method,dtype", _random_cases())
+def test_random_shapes_and_methods(shape, method, dtype):
+    """Random ragged shapes (tall and wide) through every method, against the
+    C++ reference's standard result (all methods agree with it in fp64)."""
+    print(f"ns random {shape} method {method} {dtype}", flush=True)
+    G = _input(*shape, dtype, seed=shape[0] * 7 + shape[1] + method)
+    O = f64(_run(G, method=method))
+    ref = cref.orthogonalize(f64(G), method="standard")
+    e = rel(O, ref)
+    assert e <= TOL[dtype], e
+    if dtype == torch.bfloat16:
+        assert block_rel_max(O, ref) <= BLOCK_TOL_BF16
