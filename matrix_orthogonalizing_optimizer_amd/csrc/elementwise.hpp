@@ -51,6 +51,32 @@ template <typename T> __device__ __forceinline__ void st8(T* p, const float (&v)
   }
 }
 
+// 4 consecutive elements of T at p (8-byte aligned for 16-bit T, 16 for fp32)
+// <-> 4 floats, streaming.
+template <typename T> __device__ __forceinline__ void ld4(const T* p, float (&v)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x2 w = __builtin_nontemporal_load(as_global(reinterpret_cast<const u32x2*>(p)));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = to_f32(__builtin_bit_cast(T, (uint16_t)(w[e >> 1] >> ((e & 1) * 16))));
+  } else {
+    const f32x4 x = __builtin_nontemporal_load(as_global(reinterpret_cast<const f32x4*>(p)));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = x[e];
+  }
+}
+
+template <typename T> __device__ __forceinline__ void st4(T* p, const float (&v)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    u32x2 w;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      w[j] = (uint32_t)bits16(from_f32<T>(v[2 * j])) | ((uint32_t)bits16(from_f32<T>(v[2 * j + 1])) << 16);
+    __builtin_nontemporal_store(w, as_global(reinterpret_cast<u32x2*>(p)));
+  } else {
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, as_global(reinterpret_cast<f32x4*>(p)));
+  }
+}
+
 template <typename TG, typename TX>
 __global__ __launch_bounds__(256) void momentum_kernel(const MomArgs a) {
   constexpr int CGS = KM_TC / 8;    // 8-column groups per tile row
@@ -163,12 +189,15 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MomArgs a) {
 // one row per wave), each wave covering 512 consecutive columns of a row (1
 // KB of a 16-bit G, 2 KB of M), so that a workgroup's accesses fall in few
 // DRAM pages (14336 x 4096 units: 8.14 ms per 64-unit bucket against
-// 8.50-8.73 with 8 x 512 tiles and 8.37 with 16 x 512).  One partial sum of
-// U^2 per workgroup.
+// 8.50-8.73 with 8 x 512 tiles and 8.37 with 16 x 512).  A lane takes
+// 4-element pieces (columns 4 l .. 4 l + 3 and 256 further on), so every
+// load and store instruction of a wave covers one contiguous range, as in
+// the AdamW kernel.  One partial sum of U^2 per workgroup.
 template <typename TG, typename TX>
 __global__ __launch_bounds__(256) void momentum_rows_kernel(const MomArgs a) {
-  constexpr int NHR = KMR_TR / 4;  // rows per thread (4 waves, one row each per pass)
-  static_assert(KMR_TR % 4 == 0 && KMR_TC == 512, "tile shape");
+  constexpr int NHR = KMR_TR / 4;   // rows per thread (4 waves, one row each per pass)
+  constexpr int NP = KMR_TC / 256;  // 4-element pieces per lane and row
+  static_assert(KMR_TR % 4 == 0 && KMR_TC % 256 == 0, "tile shape");
   __shared__ float red[4];
   const int unit = blockIdx.x / a.tilesPerUnit;
   const int t = blockIdx.x - unit * a.tilesPerUnit;
@@ -179,26 +208,27 @@ __global__ __launch_bounds__(256) void momentum_rows_kernel(const MomArgs a) {
   TX* __restrict__ X = reinterpret_cast<TX*>(a.D) + (int64_t)unit * a.sD;
 
   const int tid = threadIdx.x;
-  const int c = tc * KMR_TC + (tid & 63) * 8;
-  const bool cin = c < a.cols;
-  const bool full = a.vec_ok && c + 8 <= a.cols;
-  float g[NHR][8], m[NHR][8];
+  float g[NHR][NP][4], m[NHR][NP][4];
 #pragma unroll
   for (int h = 0; h < NHR; ++h) {
     const int r = tr * KMR_TR + (tid >> 6) + 4 * h;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { g[h][e] = 0.f; m[h][e] = 0.f; }
-    if (r < a.rows && cin) {
-      const int64_t off = (int64_t)r * d.ld + c;
-      if (full) {
-        ld8(G + off, g[h]);
-        if (M) ld8(M + off, m[h]);
-      } else {
+    for (int p = 0; p < NP; ++p) {
+      const int c = tc * KMR_TC + p * 256 + (tid & 63) * 4;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (c + e < a.cols) {
-            g[h][e] = to_f32(G[off + e]);
-            if (M) m[h][e] = M[off + e];
+      for (int e = 0; e < 4; ++e) { g[h][p][e] = 0.f; m[h][p][e] = 0.f; }
+      if (r < a.rows && c < a.cols) {
+        const int64_t off = (int64_t)r * d.ld + c;
+        if (a.vec_ok && c + 4 <= a.cols) {
+          ld4(G + off, g[h][p]);
+          if (M) ld4(M + off, m[h][p]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (c + e < a.cols) {
+              g[h][p][e] = to_f32(G[off + e]);
+              if (M) m[h][p][e] = M[off + e];
+            }
           }
         }
       }
@@ -208,31 +238,34 @@ __global__ __launch_bounds__(256) void momentum_rows_kernel(const MomArgs a) {
 #pragma unroll
   for (int h = 0; h < NHR; ++h) {
     const int r = tr * KMR_TR + (tid >> 6) + 4 * h;
-    float u[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (M) {
-        const float mn = fmaf(a.mu, m[h][e], g[h][e]);
-        m[h][e] = mn;
-        u[e] = a.nesterov ? fmaf(a.mu, mn, g[h][e]) : mn;
-      } else {
-        u[e] = g[h][e];
+    for (int p = 0; p < NP; ++p) {
+      const int c = tc * KMR_TC + p * 256 + (tid & 63) * 4;
+      float u[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (M) {
+          const float mn = fmaf(a.mu, m[h][p][e], g[h][p][e]);
+          m[h][p][e] = mn;
+          u[e] = a.nesterov ? fmaf(a.mu, mn, g[h][p][e]) : mn;
+        } else {
+          u[e] = g[h][p][e];
+        }
+        ss = fmaf(u[e], u[e], ss);
       }
-      ss = fmaf(u[e], u[e], ss);
-    }
-    if (r < a.rows && cin) {
-      const int64_t off = (int64_t)r * d.ld + c;
-      if (M) {
-        if (full) {
-          st8(M + off, m[h]);
+      if (r < a.rows && c < a.cols && M) {
+        const int64_t off = (int64_t)r * d.ld + c;
+        if (a.vec_ok && c + 4 <= a.cols) {
+          st4(M + off, m[h][p]);
         } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (c + e < a.cols) M[off + e] = m[h][e];
+          for (int e = 0; e < 4; ++e)
+            if (c + e < a.cols) M[off + e] = m[h][p][e];
         }
       }
-      // columns past cols within the chunk are the layout's zero padding
-      st8(X + (int64_t)r * a.ldd + c, u);
+      // the working copy's zero padding up to ldd (a multiple of 8) is
+      // written here too: u is zero past cols
+      if (r < a.rows && c < a.ldd) st4(X + (int64_t)r * a.ldd + c, u);
     }
   }
   const float s = block_sum_256(ss, red);
@@ -272,39 +305,46 @@ __device__ __forceinline__ void adam_elem(float& w, float g, float& m, float& v,
   w = w * a.keep - a.step * (m / (a.eps + sqrtf(v)));
 }
 
+// A workgroup's ADAM_EPB elements in pieces of 4 per lane: lane l of a pass
+// takes elements 4 l .. 4 l + 3 of its wave's 256, so every load and store
+// instruction of a wave covers one contiguous range (512 bytes of a 16-bit
+// tensor, 1 KB of an fp32 one).  With 8 elements per lane the fp32 moments
+// took two 16-byte pieces 32 bytes apart per lane, each instruction touching
+// twice the cache lines: 6% slower (5.26 against 5.58 TB/s on the
+// Llama-3-8B-shaped AdamW set).
 template <typename TW>
 __device__ __forceinline__ void adamw_tile(const AdamDesc& d, int64_t base, const AdamArgs& a) {
-  constexpr int NCH = ADAM_EPB / (256 * 8);  // 8-element chunks per thread
+  constexpr int NCH = ADAM_EPB / (256 * 4);  // 4-element pieces per thread
   TW* __restrict__ W = reinterpret_cast<TW*>(d.w);
   const TW* __restrict__ G = reinterpret_cast<const TW*>(d.g);
   int64_t i0[NCH];
   bool vec[NCH];
 #pragma unroll
   for (int it = 0; it < NCH; ++it) {
-    i0[it] = base + (int64_t)(it * 256 + threadIdx.x) * 8;
-    vec[it] = d.vec_ok && i0[it] + 8 <= d.numel;
+    i0[it] = base + (int64_t)(it * 256 + threadIdx.x) * 4;
+    vec[it] = d.vec_ok && i0[it] + 4 <= d.numel;
   }
   // every load of the tile is issued before the first use
-  float w[NCH][8], g[NCH][8], m[NCH][8], v[NCH][8];
+  float w[NCH][4], g[NCH][4], m[NCH][4], v[NCH][4];
 #pragma unroll
   for (int it = 0; it < NCH; ++it) {
     if (vec[it]) {
-      ld8(W + i0[it], w[it]);
-      ld8(G + i0[it], g[it]);
-      ld8(d.m + i0[it], m[it]);
-      ld8(d.v + i0[it], v[it]);
+      ld4(W + i0[it], w[it]);
+      ld4(G + i0[it], g[it]);
+      ld4(d.m + i0[it], m[it]);
+      ld4(d.v + i0[it], v[it]);
     }
   }
 #pragma unroll
   for (int it = 0; it < NCH; ++it) {
     if (vec[it]) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) adam_elem(w[it][e], g[it][e], m[it][e], v[it][e], a);
-      st8(W + i0[it], w[it]);
-      st8(d.m + i0[it], m[it]);
-      st8(d.v + i0[it], v[it]);
+      for (int e = 0; e < 4; ++e) adam_elem(w[it][e], g[it][e], m[it][e], v[it][e], a);
+      st4(W + i0[it], w[it]);
+      st4(d.m + i0[it], m[it]);
+      st4(d.v + i0[it], v[it]);
     } else {
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 4; ++e) {
         const int64_t i = i0[it] + e;
         if (i >= d.numel) break;
         float wi = to_f32(W[i]), gi = to_f32(G[i]), mi = d.m[i], vi = d.v[i];
