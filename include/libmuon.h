@@ -259,7 +259,8 @@ muon_status muon_step(const muon_plan* plan, const muon_param_ptrs* ptrs, int32_
  * in place: X <- NS_steps(X / ||X||_F) ([Blog] "Newton-Schulz Iteration":
  * X <- a_k X + (b_k A + c_k A^2) X with A = X X^T), a tall X being processed
  * as its transpose ([Blog] "Sign of a Matrix"); method standard, Gram
- * ([DeepSpeed]; resolved as described above) or auto.
+ * ([DeepSpeed]; resolved as described above), auto, or the restarted Gram
+ * chain (an extension, resolved as described above).
  * coeffs: host array of steps x 3 floats as in muon_hparams, or NULL.  A
  * zero matrix stays zero.  workspace: device memory of at least
  * ns_orthogonalize_workspace_bytes bytes, owned by the caller, contents
